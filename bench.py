@@ -1,0 +1,187 @@
+"""Benchmark of the RSM mixer hot path on one MI355X.
+
+A step is one rsm_forward_chunked call (route, sparse decay, chunk contractions, state
+scan, emit) over one batch of the 400M-scale layer workload: B=8, T=2048, Hh=8, M=64,
+Dv=128, top-16, C=64, bf16 q/k/z/v, fp32 f/state/outputs.  Three input sets are rotated
+so the ~154 MB working set cannot sit in the 256 MB last-level cache between steps.
+The decode step (256 sequences x 16 heads, M64 Dv128 K16, prefill T=512) is timed in the
+same run: 1024 back-to-back rsm_decode_step calls between two HIP events.
+
+Prints one JSON line.  Inputs are synthetic (seeded generator), already resident in HBM
+when the timed region starts.  `--gpus N` with N > 1 is refused: this build is one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RSM forward tokens/s (B8 T2048 M64) + decode-step µs; % HBM/MFMA roofline"
+PEAK_HBM_GBS = 8000.0
+
+
+def forward_bytes(B, T, Hh, M, Dv, es):
+    """Algorithmic bytes of one forward: every input read once, outputs written once."""
+    return (3 * B * T * Hh * M * es + B * T * Hh * Dv * es + B * T * Hh * 4
+            + B * T * Hh * Dv * 4 + B * Hh * M * Dv * 4)
+
+
+def decode_bytes(B, Hh, M, Dv, K, es):
+    """Per step: full state read, K rows written back, inputs read, o written."""
+    return (B * Hh * M * Dv * 4 + B * Hh * K * Dv * 4 + 3 * B * Hh * M * es + B * Hh * Dv * es
+            + B * Hh * 4 + B * Hh * Dv * 4)
+
+
+def to_dev(d, torch):
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return {"q": t(d["q"]), "k": t(d["k"]), "z": t(d["z"]), "v": t(d["v"]),
+            "f": torch.from_numpy(d["f"]).cuda()}
+
+
+def cpu_baseline(w, d):
+    """The float64 oracle, as is, on the host cores: the full forward workload."""
+    from oracle import oracle
+    from sparse_routed_slot_amd import inputs as gen
+    r = {n: gen.as_f64(d[n], "bf16") for n in "qkzv"}
+    f = d["f"].astype(np.float64)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.forward(r["q"], r["k"], r["z"], r["v"], f, w.K)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full forward workload (B{w.B} T{w.T} Hh{w.Hh} M{w.M} Dv{w.Dv} K{w.K}), "
+                      f"float64 recurrence, {dt:.2f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_routed_slot_amd import inputs as gen
+    from sparse_routed_slot_amd import rsm
+
+    if not os.path.exists(rsm.lib_path()):
+        from sparse_routed_slot_amd import build
+        build.build_library()
+    rsm.load()
+    torch.cuda.set_device(0)
+
+    # ---------------------------------------------------------------- forward
+    w = gen.WORKLOADS["fwd_b8_t2048"]
+    print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
+    host_sets = [gen.make_inputs(w.B, w.T, w.Hh, w.M, w.Dv, w.dtype, w.seed + 100 * i) for i in range(3)]
+    sets = [to_dev(d, torch) for d in host_sets]
+    o = torch.empty((w.B, w.T, w.Hh, w.Dv), dtype=torch.float32, device="cuda")
+    Hs = torch.empty((w.B, w.Hh, w.M, w.Dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(rsm.forward_workspace_bytes(torch.bfloat16, w.B, w.T, w.Hh, w.M, w.Dv, w.C),
+                     dtype=torch.uint8, device="cuda")
+
+    def fwd(i):
+        s = sets[i % len(sets)]
+        rsm.forward_chunked(s["q"], s["k"], s["z"], s["v"], s["f"], w.K, C=w.C, workspace=ws, out=o,
+                            state_out=Hs)
+
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = float(np.mean(per_call_ms))
+    tok = w.B * w.T
+    fbytes = forward_bytes(w.B, w.T, w.Hh, w.M, w.Dv, 2)
+    achieved = fbytes / (kernel_ms * 1e-3) / 1e9
+    print(f"[bench] forward: wall {ms_per_step * 1e3:.1f} us/step, events {kernel_ms * 1e3:.1f} us "
+          f"(min {min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- decode
+    wd = gen.WORKLOADS["decode_b256"]
+    print(f"[bench] decode: prefill T={wd.T} for {wd.B}x{wd.Hh} heads", file=sys.stderr, flush=True)
+    dd = gen.make_inputs(wd.B, wd.T, wd.Hh, wd.M, wd.Dv, wd.dtype, wd.seed)
+    pre = to_dev(dd, torch)
+    del dd
+    _, Hdec, _ = rsm.forward_chunked(pre["q"], pre["k"], pre["z"], pre["v"], pre["f"], wd.K, C=wd.C)
+    del pre
+    rng = np.random.default_rng(1000 + wd.seed)
+    pool = [to_dev(gen.decode_step_inputs(rng, wd.B, wd.Hh, wd.M, wd.Dv, "bf16"), torch) for _ in range(16)]
+    od = torch.empty((wd.B, wd.Hh, wd.Dv), dtype=torch.float32, device="cuda")
+
+    def dec(i):
+        s = pool[i % len(pool)]
+        rsm.decode_step(s["q"], s["k"], s["z"], s["v"], s["f"], Hdec, wd.K, out=od)
+
+    for i in range(16):
+        dec(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.decode_steps):
+        dec(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    dbytes = decode_bytes(wd.B, wd.Hh, wd.M, wd.Dv, wd.K, 2)
+    print(f"[bench] decode: {dec_us:.2f} us/step, {dbytes / (dec_us * 1e-6) / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": METRIC,
+        "value": tok / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hh": w.Hh, "M": w.M, "Dv": w.Dv, "K": w.K,
+                   "C": w.C, "inputs": "bf16 q,k,z,v; fp32 f, state, outputs", "input_sets_rotated": 3},
+        "decode_us_per_step": dec_us,
+        "decode_config": {"workload": wd.name, "B": wd.B, "Hh": wd.Hh, "M": wd.M, "Dv": wd.Dv, "K": wd.K,
+                          "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": len(pool)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "rsm_forward_chunked = fwd_prep_kernel + fwd_scan_kernel",
+                     "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
+        "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                            "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, host_sets[0])
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,125 @@
+/*
+ * rsm.h -- C ABI of librsm.so: the Routing State Model (RSM) mixer of Raven on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Per head the mixer keeps a slot memory H of M slots x Dv columns.  For every token
+ * it scores the M slots with a sigmoid of the router logits z, keeps the top K scores
+ * (ties go to the lower slot index), decays and writes only those slots, and reads the
+ * memory with the query (Raven README page, "How Raven Works" listing):
+ *
+ *     s      = TopK(sigmoid(z))                      (zeros outside the top K)
+ *     alpha  = exp(s * f)                            (1, i.e. untouched, outside the top K)
+ *     H[i,:] = alpha_i * H[i,:] + (1 - alpha_i) * k_i * v     for the selected slots i
+ *     o      = q . H = sum_i q_i * H[i,:]            (read after the update)
+ *
+ * Unselected slots keep their exact bits (Raven paper summary, section 4.1 and appendix
+ * A.7).  The chunked forward evaluates the same recurrence chunk by chunk (appendix
+ * A.5: T split into chunks of length C) with per-slot cumulative log-decay taken from
+ * the chunk start.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, contiguous, row-major device buffers in the shapes given.
+ *    q, k, z are [.., M]; v is [.., Dv]; f is one fp32 scalar per token and head and
+ *    must be <= 0 (-inf allowed: full overwrite of the selected slots).
+ *  - dtype selects the element type of q, k, z, v: RSM_F32 (float) or RSM_BF16
+ *    (bfloat16 bits).  f, states and outputs are always fp32.
+ *  - The caller owns every buffer.  The library keeps no global mutable state and
+ *    allocates no device memory; calls are asynchronous on `stream` (a hipStream_t,
+ *    NULL = the default stream) and return after enqueueing.
+ *  - Errors: argument errors return a negative rsm_status before anything is enqueued;
+ *    a failed launch returns RSM_ERR_HIP.  Data values are not validated: f > 0, NaN or
+ *    infinite z/q/k/v give unspecified results.
+ *  - Supported shapes: M in {16, 32, 64, 128}; Dv in {16, 32, 64, 128, 256};
+ *    1 <= K <= M; chunk C in {16, 32, 64}; B, T, Hh >= 0 (T need not be a multiple of C;
+ *    an empty call enqueues nothing except copying H0, or zeros, into H_out).
+ */
+#ifndef RSM_H
+#define RSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RSM_F32 = 0, RSM_BF16 = 1 } rsm_dtype;
+
+typedef enum {
+    RSM_OK = 0,
+    RSM_ERR_NULL = -1,        /* a required pointer is NULL */
+    RSM_ERR_SHAPE = -2,       /* a size is negative or outside the supported set */
+    RSM_ERR_K = -3,           /* K outside [1, M] */
+    RSM_ERR_DTYPE = -4,       /* dtype is not RSM_F32 / RSM_BF16 */
+    RSM_ERR_UNSUPPORTED = -5, /* a combination the library was not built for */
+    RSM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the queried size */
+    RSM_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
+    RSM_ERR_ALIAS = -8        /* an output overlaps an input it must not overlap */
+} rsm_status;
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* rsm_status_string(int status);
+
+/* Version of this ABI (major*10000 + minor*100 + patch). */
+int rsm_abi_version(void);
+
+/*
+ * Router: sigmoid scores, top K per token-head row (RSM router, "How Raven Works":
+ * TopK(sigmoid(r_proj(x))); the logits z are taken as given).
+ *   z     [B,T,Hh,M]  dtype          router logits
+ *   idx   [B,T,Hh,K]  int32  out     selected slots, ascending slot order
+ *   score [B,T,Hh,K]  fp32   out     sigmoid(z) at those slots; may be NULL
+ * Ranking is on z (equivalent to ranking the exact sigmoid, which is strictly
+ * increasing); equal logits (-0 == +0) go to the lower slot index.
+ */
+int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
+                   int64_t K, int32_t* idx, float* score, void* stream);
+
+/*
+ * Bytes of device workspace rsm_forward_chunked needs for these sizes (0 if T == 0).
+ * Returns 0 and leaves nothing to allocate for unsupported shapes as well; the
+ * forward call then reports the shape error.
+ */
+size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
+                                   int64_t Dv, int64_t C);
+
+/*
+ * Chunked forward over a whole sequence (RSM update and read of "How Raven Works",
+ * evaluated chunkwise as in the Raven paper's appendix A.5).
+ *   q, k, z  [B,T,Hh,M]   dtype
+ *   v        [B,T,Hh,Dv]  dtype
+ *   f        [B,T,Hh]     fp32, <= 0 (-inf allowed)
+ *   H0       [B,Hh,M,Dv]  fp32 initial state, or NULL for a zero state
+ *   o        [B,T,Hh,Dv]  fp32 out (must not overlap any input)
+ *   H_out    [B,Hh,M,Dv]  fp32 out final state, or NULL; may be the same buffer as H0
+ *   idx_out  [B,T,Hh,K]   int32 out selected slots (ascending), or NULL
+ *   workspace/workspace_bytes: device scratch of at least
+ *            rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C) bytes (owned by the
+ *            caller, contents undefined on entry and on return)
+ * Slots never selected in the sequence come back in H_out bit-identical to H0.
+ */
+int rsm_forward_chunked(const void* q, const void* k, const void* z, const void* v, int dtype,
+                        const float* f, const float* H0, int64_t B, int64_t T, int64_t Hh,
+                        int64_t M, int64_t Dv, int64_t K, int64_t C, float* o, float* H_out,
+                        int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent step for B x Hh heads (fused route + update + read; the README's
+ * "fused recurrent kernels for generation").
+ *   q, k, z  [B,Hh,M]     dtype
+ *   v        [B,Hh,Dv]    dtype
+ *   f        [B,Hh]       fp32, <= 0 (-inf allowed)
+ *   H        [B,Hh,M,Dv]  fp32 state, updated in place: only the K selected rows of
+ *                         each head are written, every other row keeps its bits
+ *   o        [B,Hh,Dv]    fp32 out, read after the update
+ *   idx_out  [B,Hh,K]     int32 out selected slots (ascending), or NULL
+ */
+int rsm_decode_step(const void* q, const void* k, const void* z, const void* v, int dtype,
+                    const float* f, float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv,
+                    int64_t K, float* o, int32_t* idx_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSM_H */

@@ -1,0 +1,172 @@
+// rsm_decode.hip -- fused recurrent decode step (route + sparse update + read) for one
+// token of every head.
+//
+// Raven README page, "How Raven Works": per token, the top-K slots by sigmoid score are
+// decayed by alpha = exp(s*f) and written with (1-alpha)*k_i*v; o = q . H is read after
+// the update; the README names "fused recurrent kernels for generation" for this case.
+//
+// One workgroup (256 threads) per head.  The fp32 state H [M, Dv] is streamed once as
+// float4 rows (Dv/4 threads per row); the loads are issued before the router runs so
+// the HBM latency overlaps with the top-K.  Wave 0 routes the M logits (lane = slot) and
+// publishes alpha, (1-alpha)*k and q per slot in LDS.  Every thread then updates the
+// selected rows it holds in registers, writes back only those rows, and accumulates its
+// partial read q_i*H[i,:]; a reduction over row groups in LDS finishes o.
+#include "rsm_device.h"
+#include "rsm_launch.h"
+
+namespace rsm {
+
+template <typename T, int M, int DV>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ z, const T* __restrict__ v,
+    const float* __restrict__ f, float* __restrict__ H, int K, float* __restrict__ o,
+    int32_t* __restrict__ idx_out) {
+    constexpr int SPL = M > kWave ? M / kWave : 1;
+    constexpr int NB = Elem<T>::kKeyBits;
+    constexpr int TPR = DV / 4;               // threads per state row, one float4 each
+    constexpr int RPP = 256 / TPR;            // rows covered per pass of the workgroup
+    constexpr int RPT = (M + RPP - 1) / RPP;  // rows held per thread
+    __shared__ float s_a[M], s_wk[M], s_q[M];
+    __shared__ int s_upd[M];
+    __shared__ float4 s_red[RPP][TPR];
+
+    const long bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int cg = tid % TPR, rg = tid / TPR;
+    float* Hb = H + bh * long(M) * DV;
+
+    float4 hv[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int row = rg + j * RPP;
+        if (row < M) hv[j] = *reinterpret_cast<const float4*>(Hb + row * DV + 4 * cg);
+    }
+    const T* vb = v + bh * DV + 4 * cg;
+    const float4 vv = make_float4(Elem<T>::load(vb, 0), Elem<T>::load(vb, 1), Elem<T>::load(vb, 2),
+                                  Elem<T>::load(vb, 3));
+
+    if (tid < kWave) {
+        const int lane = tid;
+        const T* zb = z + bh * M;
+        uint32_t key[SPL];
+        float zv[SPL];
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            const int slot = r * kWave + lane;
+            zv[r] = slot < M ? Elem<T>::load(zb, slot) : 0.0f;
+            key[r] = slot < M ? order_key<NB>(zv[r]) : 0u;
+        }
+        bool sel[SPL];
+        wave_topk<SPL, NB>(key, K, sel);
+        const float ft = f[bh];
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            const int slot = r * kWave + lane;
+            if (slot < M) {
+                float a = 1.0f, wk = 0.0f;
+                int upd = 0;
+                if (sel[r]) {
+                    const float s = sigmoidf_dev(zv[r]);
+                    if (s > 0.0f) a = __expf(s * ft);
+                    if (a != 1.0f) {
+                        upd = 1;
+                        wk = (1.0f - a) * Elem<T>::load(k + bh * M, slot);
+                    }
+                }
+                s_a[slot] = a;
+                s_wk[slot] = wk;
+                s_upd[slot] = upd;
+                s_q[slot] = Elem<T>::load(q + bh * M, slot);
+            }
+        }
+        if (idx_out) {
+            int pos[SPL];
+            wave_compact<SPL>(sel, pos);
+#pragma unroll
+            for (int r = 0; r < SPL; ++r)
+                if (sel[r]) idx_out[bh * K + pos[r]] = r * kWave + lane;
+        }
+    }
+    __syncthreads();
+
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int row = rg + j * RPP;
+        if (row < M) {
+            float4 h = hv[j];
+            if (s_upd[row]) {
+                const float a = s_a[row], wk = s_wk[row];
+                h.x = fmaf(a, h.x, wk * vv.x);
+                h.y = fmaf(a, h.y, wk * vv.y);
+                h.z = fmaf(a, h.z, wk * vv.z);
+                h.w = fmaf(a, h.w, wk * vv.w);
+                *reinterpret_cast<float4*>(Hb + row * DV + 4 * cg) = h;
+            }
+            const float qi = s_q[row];
+            acc.x = fmaf(qi, h.x, acc.x);
+            acc.y = fmaf(qi, h.y, acc.y);
+            acc.z = fmaf(qi, h.z, acc.z);
+            acc.w = fmaf(qi, h.w, acc.w);
+        }
+    }
+    s_red[rg][cg] = acc;
+    __syncthreads();
+    if (rg == 0) {
+        float4 sum = s_red[0][cg];
+        for (int g = 1; g < RPP; ++g) {
+            const float4 p = s_red[g][cg];
+            sum.x += p.x;
+            sum.y += p.y;
+            sum.z += p.z;
+            sum.w += p.w;
+        }
+        *reinterpret_cast<float4*>(o + bh * DV + 4 * cg) = sum;
+    }
+}
+
+template <typename T, int M, int DV>
+static int launch_decode_mdv(const T* q, const T* k, const T* z, const T* v, const float* f, float* H,
+                             long n_heads, int K, float* o, int32_t* idx_out, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<T, M, DV>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
+                       k, z, v, f, H, K, o, idx_out);
+    return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
+}
+
+template <typename T, int M>
+static int launch_decode_m(const T* q, const T* k, const T* z, const T* v, const float* f, float* H,
+                           long n_heads, int Dv, int K, float* o, int32_t* idx_out, hipStream_t s) {
+    switch (Dv) {
+        case 16: return launch_decode_mdv<T, M, 16>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+        case 32: return launch_decode_mdv<T, M, 32>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+        case 64: return launch_decode_mdv<T, M, 64>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+        case 128: return launch_decode_mdv<T, M, 128>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+        case 256: return launch_decode_mdv<T, M, 256>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+    }
+    return RSM_ERR_UNSUPPORTED;
+}
+
+template <typename T>
+static int launch_decode(const void* q, const void* k, const void* z, const void* v, const float* f,
+                         float* H, long n_heads, int M, int Dv, int K, float* o, int32_t* idx_out,
+                         hipStream_t s) {
+    const T *qq = static_cast<const T*>(q), *kk = static_cast<const T*>(k), *zz = static_cast<const T*>(z),
+            *vv = static_cast<const T*>(v);
+    switch (M) {
+        case 16: return launch_decode_m<T, 16>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
+        case 32: return launch_decode_m<T, 32>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
+        case 64: return launch_decode_m<T, 64>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
+        case 128: return launch_decode_m<T, 128>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
+    }
+    return RSM_ERR_UNSUPPORTED;
+}
+
+int decode_step_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
+                       const float* f, float* H, long n_heads, int M, int Dv, int K, float* o,
+                       int32_t* idx_out, hipStream_t stream) {
+    if (n_heads == 0) return RSM_OK;
+    if (dtype == RSM_F32) return launch_decode<float>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, stream);
+    return launch_decode<bf16_t>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, stream);
+}
+
+}  // namespace rsm

@@ -1,0 +1,111 @@
+// rsm_device.h -- device-side building blocks shared by the librsm kernels (gfx950).
+//
+// Element access for the two input types, the order-preserving integer key used by
+// the router, the wave64 exact top-K, and the MFMA fragment types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rsm {
+
+constexpr int kWave = 64;
+
+// bfloat16 is carried as its 16 raw bits.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bfloat16, round to nearest even (finite inputs; infinities stay infinite).
+__device__ __forceinline__ uint16_t float_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kKeyBits = 32;
+    __device__ static __forceinline__ float load(const float* p, long i) { return p[i]; }
+};
+template <> struct Elem<bf16_t> {
+    static constexpr int kKeyBits = 16;
+    __device__ static __forceinline__ float load(const bf16_t* p, long i) {
+        return bf16_to_float(p[i].bits);
+    }
+};
+
+// Order-preserving unsigned key of a float: a < b  <=>  key(a) < key(b), with -0 == +0.
+// For bf16-representable values only the top 16 bits carry information.
+template <int NB>
+__device__ __forceinline__ uint32_t order_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return NB == 32 ? u : (u >> (32 - NB));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
+
+// Number of set bits of m in lanes below the calling lane.
+__device__ __forceinline__ int mbcnt64(unsigned long long m) {
+    return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
+}
+
+// Exact top-K of one row of M <= 64*SPL slots spread over a wave: slot r*64 + lane is held
+// in key[r] (0 for lanes past M; every real value has a key >= 1).  A slot is selected iff
+// fewer than K slots rank before it, ranking by key descending then slot index ascending.
+//
+// The K-th largest key is found by a bitwise search from the top bit: keep the candidate
+// bit if at least K keys are >= the candidate.  The search stops early once exactly K keys
+// are >= the candidate (that set is then the answer, with no tie across its boundary).
+// Ties at the threshold are resolved by slot order with a prefix count over the wave.
+template <int SPL, int NB>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[SPL], int K, bool (&sel)[SPL]) {
+    uint32_t th = 0;
+#pragma unroll 1
+    for (int bit = NB - 1; bit >= 0; --bit) {
+        const uint32_t cand = th | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) cnt += popc64(__ballot(key[r] >= cand));
+        if (cnt >= K) th = cand;
+        if (cnt == K) break;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) gt += popc64(__ballot(key[r] > th));
+    const int need = K - gt;
+    int before = 0;
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) {
+        const unsigned long long eq = __ballot(key[r] == th);
+        const int rank = before + mbcnt64(eq);
+        sel[r] = key[r] > th || (key[r] == th && rank < need);
+        before += popc64(eq);
+    }
+}
+
+// Position of each selected slot in the ascending list of selected slots.
+template <int SPL>
+__device__ __forceinline__ void wave_compact(const bool (&sel)[SPL], int (&pos)[SPL]) {
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) {
+        const unsigned long long m = __ballot(sel[r]);
+        pos[r] = base + mbcnt64(m);
+        base += popc64(m);
+    }
+}
+
+__device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// MFMA fragment types (16x16 output tiles).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+}  // namespace rsm

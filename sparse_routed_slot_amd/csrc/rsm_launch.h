@@ -1,0 +1,32 @@
+// rsm_launch.h -- host-side launchers implemented by the kernel sources and called by the
+// C ABI layer (rsm_api.hip).  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rsm.h"
+
+namespace rsm {
+
+int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx,
+                      float* score, hipStream_t stream);
+
+int decode_step_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
+                       const float* f, float* H, long n_heads, int M, int Dv, int K, float* o,
+                       int32_t* idx_out, hipStream_t stream);
+
+// Workspace of the chunked forward: byte offsets of its regions and the total.
+struct FwdLayout {
+    size_t tiles_off, elast_off, flags_off, total;
+    long n_chunks;
+};
+FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C);
+
+int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
+                           const float* f, const float* H0, long B, long T, long Hh, int M,
+                           int Dv, int K, int C, float* o, float* H_out, int32_t* idx_out,
+                           void* workspace, hipStream_t stream);
+
+}  // namespace rsm

@@ -33,12 +33,14 @@ __all__ = [
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 array -> uint16 bf16 bit patterns, round-to-nearest-even (NaN kept quiet)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    u = x.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                    # no wrap-around: finite values and infinities stay below 2^32
+    r >>= np.uint32(16)
     nan = np.isnan(x)
     if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint32)
+        r[nan] = (u[nan] >> 16) | np.uint32(0x40)
     return r.astype(np.uint16)
 
 

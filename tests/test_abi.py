@@ -1,0 +1,119 @@
+"""The C ABI library loads, exports every symbol ``include/rsm.h`` declares, and rejects
+bad arguments with the documented status codes before any GPU work (CPU-only: no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "rsm.h")
+LIB = os.path.join(ROOT, "sparse_routed_slot_amd", "librsm.so")
+
+OK, NULL, SHAPE, KERR, DTYPE, UNSUP, WS, HIP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from sparse_routed_slot_amd import build
+        build.build_library()
+    L = ctypes.CDLL(LIB)
+    L.rsm_status_string.restype = ctypes.c_char_p
+    L.rsm_route_topk.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, I64, P, P, P]
+    L.rsm_forward_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, I64]
+    L.rsm_forward_workspace_bytes.restype = ctypes.c_size_t
+    L.rsm_forward_chunked.argtypes = [P, P, P, P, ctypes.c_int, P, P, I64, I64, I64, I64, I64, I64, I64,
+                                      P, P, P, P, ctypes.c_size_t, P]
+    L.rsm_decode_step.argtypes = [P, P, P, P, ctypes.c_int, P, P, I64, I64, I64, I64, I64, P, P, P]
+    return L
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rsm_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"rsm_route_topk", "rsm_forward_chunked", "rsm_decode_step"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in rsm.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in (OK, NULL, SHAPE, KERR, DTYPE, UNSUP, WS, HIP, ALIAS):
+        assert lib.rsm_status_string(s)
+    assert lib.rsm_status_string(12345) == b"unknown status"
+
+
+A, B_, C_, D_, E_, F_, G_ = (P(0x10000 * (i + 1)) for i in range(7))
+
+
+def route(lib, z=A, dtype=1, B=1, T=4, Hh=2, M=64, K=4, idx=B_, score=None):
+    return lib.rsm_route_topk(z, dtype, B, T, Hh, M, K, idx, score, None)
+
+
+def test_route_argument_errors(lib):
+    assert route(lib, dtype=7) == DTYPE
+    assert route(lib, M=48) == SHAPE
+    assert route(lib, B=-1) == SHAPE
+    assert route(lib, K=0) == KERR
+    assert route(lib, K=65) == KERR
+    assert route(lib, z=None) == NULL
+    assert route(lib, idx=None) == NULL
+    assert route(lib, idx=P(0x10000 + 8)) == ALIAS    # idx overlaps z
+    assert route(lib, B=0) == OK                       # empty: nothing enqueued
+    assert route(lib, T=0, z=None, idx=None) == OK
+
+
+def fwd(lib, dtype=1, B=1, T=100, Hh=2, M=64, Dv=128, K=8, C=64, o=F_, H0=None, H_out=None, idx=None,
+        ws=P(0x900000), wsb=1 << 30, q=A):
+    return lib.rsm_forward_chunked(q, B_, C_, D_, dtype, E_, H0, B, T, Hh, M, Dv, K, C, o, H_out, idx, ws,
+                                   wsb, None)
+
+
+def test_forward_argument_errors(lib):
+    assert fwd(lib, dtype=3) == DTYPE
+    assert fwd(lib, Dv=48) == SHAPE
+    assert fwd(lib, C=48) == SHAPE
+    assert fwd(lib, M=256) == SHAPE
+    assert fwd(lib, T=-5) == SHAPE
+    assert fwd(lib, K=0) == KERR
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, o=None) == NULL
+    assert fwd(lib, ws=None) == WS
+    assert fwd(lib, wsb=16) == WS
+    assert fwd(lib, o=A) == ALIAS                      # o on top of q
+    assert fwd(lib, H0=P(0x700000), H_out=P(0x700000 + 4)) == ALIAS  # partial overlap
+    assert fwd(lib, B=0) == OK
+
+
+def test_workspace_size(lib):
+    f = lib.rsm_forward_workspace_bytes
+    assert f(1, 8, 2048, 8, 64, 128, 64) > 0
+    assert f(1, 8, 0, 8, 64, 128, 64) == 0
+    assert f(1, 8, 2048, 8, 48, 128, 64) == 0          # unsupported M
+    # grows with T and with the element size
+    assert f(1, 1, 4096, 8, 64, 128, 64) > f(1, 1, 2048, 8, 64, 128, 64)
+    assert f(0, 1, 2048, 8, 64, 128, 64) > f(1, 1, 2048, 8, 64, 128, 64)
+    # at least the per-chunk tiles: 2 * C * M elements per (b, h, chunk)
+    assert f(1, 2, 128, 4, 64, 128, 64) >= 2 * 4 * 2 * (2 * 64 * 64 * 2)
+
+
+def dec(lib, dtype=1, B=4, Hh=2, M=64, Dv=128, K=8, H=F_, o=G_, idx=None, q=A):
+    return lib.rsm_decode_step(q, B_, C_, D_, dtype, E_, H, B, Hh, M, Dv, K, o, idx, None)
+
+
+def test_decode_argument_errors(lib):
+    assert dec(lib, dtype=2) == DTYPE
+    assert dec(lib, M=100) == SHAPE
+    assert dec(lib, Dv=96) == SHAPE
+    assert dec(lib, K=65) == KERR
+    assert dec(lib, H=None) == NULL
+    assert dec(lib, o=F_) == ALIAS                     # o on top of H
+    assert dec(lib, Hh=0) == OK

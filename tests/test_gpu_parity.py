@@ -1,0 +1,298 @@
+"""GPU parity of librsm (router, chunked forward, decode step) against the float64 oracle.
+
+Every comparison is on the same seeded inputs: top-K indices bit-exact, outputs and states
+within max|delta| <= 1e-5 * max|o| (fp32 inputs) or 2e-3 * max|o| (bf16 inputs, fp32
+state), plus the bitwise invariants of untouched slots.  All calls go through the C ABI
+(sparse_routed_slot_amd.rsm is ctypes marshalling only).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from sparse_routed_slot_amd import inputs as gen
+from tests._util import TOL, check_close, dev_inputs, f64_inputs, to_torch
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rsm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_routed_slot_amd import rsm as r
+    r.load()
+    return r
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_forward(rsm, d, K, C, want_idx=True):
+    t = dev_inputs(d, "cuda")
+    o, H, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=C, H0=t["H0"],
+                                    want_idx=want_idx)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), H.cpu().numpy(), (idx.cpu().numpy() if want_idx else None)
+
+
+def compare_forward(d, K, o, H, idx, sl=slice(None), what=""):
+    r = f64_inputs(d, sl)
+    ro, rH, ridx = oracle.forward(r["q"], r["k"], r["z"], r["v"], r["f"], K, H0=r["H0"])
+    tol = TOL[d["dtype"]]
+    assert np.array_equal(idx[sl], ridx), f"{what}: top-K indices differ"
+    scale = float(np.max(np.abs(ro)))
+    eo = check_close(o[sl], ro, scale, tol, f"{what} o")
+    eh = check_close(H[sl], rH, scale, tol, f"{what} H_final")
+    log(f"{what}: max|o|={scale:.3e} err_o={eo:.3e} ({eo / scale:.2e} rel) err_H={eh:.3e} "
+        f"(vs max|H| {eh / max(1e-30, float(np.max(np.abs(rH)))):.2e})")
+
+
+# ------------------------------------------------------------------------------- router
+ROUTE_CASES = ["tiny_f32", "fwd_b8_t2048", "long_t32768", "sweep_dense", "sweep_swa", "sweep_topk"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_workloads(rsm, name):
+    log(f"route {name}")
+    d = gen.make_workload(name)
+    K = d["K"]
+    z = to_torch(d["z"], d["dtype"], "cuda")
+    idx, score = rsm.route_topk(z, K)
+    torch.cuda.synchronize()
+    ridx, rscore = oracle.route_topk(gen.as_f64(d["z"], d["dtype"]), K)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(score.cpu().numpy(), rscore, rtol=2e-6, atol=1e-30)
+
+
+@pytest.mark.parametrize("M", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_ties_and_signed_zeros(rsm, M, dtype):
+    log(f"route ties M={M} {dtype}")
+    rng = np.random.default_rng(M)
+    z = (rng.integers(-4, 5, size=(3, 50, 4, M)) * 0.25).astype(np.float32)
+    z[rng.random(z.shape) < 0.15] = -0.0
+    z[0, 0, 0, :] = 1.0                                 # all equal
+    enc = gen.bf16_bits(z) if dtype == "bf16" else z
+    for K in sorted({1, 3, M // 2, M - 1, M}):
+        idx, _ = rsm.route_topk(to_torch(enc, dtype, "cuda"), K, want_score=False)
+        ridx, _ = oracle.route_topk(gen.as_f64(enc, dtype), K)
+        assert np.array_equal(idx.cpu().numpy(), ridx), f"K={K}"
+
+
+# ------------------------------------------------------------------------------- forward
+SMALL = [
+    # dtype, B, T, Hh, M, Dv, K, C, H0
+    ("f32", 1, 256, 2, 16, 16, 4, 16, False),
+    ("f32", 2, 200, 3, 64, 128, 16, 64, True),
+    ("bf16", 2, 200, 3, 64, 128, 16, 64, True),
+    ("bf16", 1, 150, 4, 128, 64, 8, 64, True),
+    ("bf16", 1, 100, 2, 32, 32, 5, 32, False),
+    ("bf16", 2, 77, 2, 16, 16, 4, 16, True),
+    ("f32", 1, 90, 2, 128, 64, 128, 32, True),
+    ("bf16", 1, 70, 1, 64, 256, 16, 16, True),
+    ("f32", 1, 130, 2, 32, 32, 32, 64, True),
+    ("bf16", 3, 1, 2, 64, 128, 16, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_forward_small(rsm, case):
+    dtype, B, T, Hh, M, Dv, K, C, h0 = case
+    log(f"forward small {case}")
+    d = gen.make_inputs(B, T, Hh, M, Dv, dtype, seed=zlib.crc32(repr(case).encode()) % 1000, h0=h0)
+    o, H, idx = run_forward(rsm, d, K, C)
+    compare_forward(d, K, o, H, idx, what=str(case))
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+def test_forward_chunk_size_invariance(rsm, C):
+    log(f"chunk invariance C={C}")
+    d = gen.make_inputs(2, 192, 2, 64, 128, "bf16", seed=5, h0=True)
+    o, H, idx = run_forward(rsm, d, 16, C)
+    compare_forward(d, 16, o, H, idx, what=f"C={C}")
+
+
+def test_forward_cyclic_swa_limit(rsm):
+    log("forward cyclic one-hot router, f = -inf")
+    d = gen.make_inputs(1, 300, 2, 128, 64, "bf16", seed=6, router="cyclic", h0=True)
+    o, H, idx = run_forward(rsm, d, 1, 64)
+    compare_forward(d, 1, o, H, idx, what="cyclic")
+
+
+def test_forward_unsafe_chunks_take_exact_path(rsm):
+    """Dense routing with f = -inf on every token: the decay product of every slot in a
+    chunk underflows, so every chunk is evaluated token by token with exact alphas."""
+    log("forward unsafe chunks")
+    d = gen.make_inputs(1, 160, 2, 16, 32, "f32", seed=7, h0=True)
+    d["f"][:] = -np.inf
+    d["f"][0, 40:70, 0] = -0.5                          # a mix of safe and unsafe chunks
+    o, H, idx = run_forward(rsm, d, 16, 32)
+    compare_forward(d, 16, o, H, idx, what="unsafe")
+
+
+def test_forward_never_selected_slots_bitwise(rsm):
+    log("never-selected slots keep H0 bits")
+    d = gen.make_inputs(2, 333, 2, 64, 128, "bf16", seed=8, h0=True)
+    z = gen.bf16_to_f32(d["z"]).copy()
+    z[..., 40:] -= 50.0
+    d["z"] = gen.bf16_bits(z)
+    d["H0"][..., 41, :] = -0.0
+    o, H, idx = run_forward(rsm, d, 16, 64)
+    assert idx.max() < 40
+    assert np.array_equal(H[..., 40:, :].view(np.uint32), d["H0"][..., 40:, :].view(np.uint32))
+    compare_forward(d, 16, o, H, idx, what="never-selected")
+
+
+def test_forward_deterministic(rsm):
+    log("determinism")
+    d = gen.make_inputs(2, 256, 4, 64, 128, "bf16", seed=9, h0=True)
+    a = run_forward(rsm, d, 16, 64)
+    b = run_forward(rsm, d, 16, 64)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype != np.int32 else x,
+                              y.view(np.uint32) if y.dtype != np.int32 else y)
+
+
+def test_forward_split_sequence_resumes(rsm):
+    log("forward(T1) -> forward(T2, H0=H) == forward(T1+T2)")
+    d = gen.make_inputs(2, 256, 2, 64, 128, "bf16", seed=10)
+    t = dev_inputs(d, "cuda")
+    o, H, _ = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], 16, C=64)
+    T1 = 100
+    sl1 = (slice(None), slice(0, T1))
+    sl2 = (slice(None), slice(T1, None))
+    o1, H1, _ = rsm.forward_chunked(*(t[n][sl1] for n in "qkzvf"), 16, C=64)
+    o2, H2, _ = rsm.forward_chunked(*(t[n][sl2] for n in "qkzvf"), 16, C=64, H0=H1)
+    torch.cuda.synchronize()
+    scale = float(o.abs().max())
+    check_close(torch.cat([o1, o2], 1).cpu().numpy(), o.cpu().numpy().astype(np.float64), scale, TOL["bf16"],
+                "split o")
+    check_close(H2.cpu().numpy(), H.cpu().numpy().astype(np.float64), scale, TOL["bf16"], "split H")
+
+
+def test_forward_empty(rsm):
+    log("empty sequence")
+    H0 = torch.randn(2, 3, 64, 128, device="cuda")
+    q = torch.empty(2, 0, 3, 64, device="cuda", dtype=torch.bfloat16)
+    v = torch.empty(2, 0, 3, 128, device="cuda", dtype=torch.bfloat16)
+    f = torch.empty(2, 0, 3, device="cuda")
+    o, H, idx = rsm.forward_chunked(q, q, q, v, f, 16, C=64, H0=H0, want_idx=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128) and torch.equal(H, H0)
+    o, H, _ = rsm.forward_chunked(q, q, q, v, f, 16, C=64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(H) == 0
+
+
+WORKLOADS = ["tiny_f32", "fwd_b8_t2048", "long_t32768", "sweep_dense", "sweep_swa", "sweep_topk"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_forward_workloads(rsm, name):
+    log(f"forward workload {name}")
+    d = gen.make_workload(name)
+    o, H, idx = run_forward(rsm, d, d["K"], d["C"])
+    compare_forward(d, d["K"], o, H, idx, what=name)
+
+
+# ------------------------------------------------------------------------------- decode
+DEC = [
+    # dtype, B, Hh, M, Dv, K
+    ("f32", 3, 2, 16, 16, 4),
+    ("bf16", 4, 3, 64, 128, 16),
+    ("f32", 2, 2, 128, 64, 8),
+    ("bf16", 2, 2, 32, 256, 32),
+    ("bf16", 5, 1, 128, 32, 128),
+]
+
+
+@pytest.mark.parametrize("case", DEC, ids=lambda c: "-".join(map(str, c)))
+def test_decode_steps(rsm, case):
+    dtype, B, Hh, M, Dv, K = case
+    log(f"decode {case}")
+    rng = np.random.default_rng(11)
+    H = torch.from_numpy(rng.standard_normal((B, Hh, M, Dv), dtype=np.float32)).cuda()
+    H[..., 0, :3] = -0.0
+    tol = TOL[dtype]
+    for step in range(12):
+        s = gen.decode_step_inputs(rng, B, Hh, M, Dv, dtype)
+        if step == 5:
+            s["f"][:] = -np.inf
+        Hprev = H.clone()
+        t = {n: to_torch(s[n], dtype, "cuda") for n in "qkzv"}
+        o, idx = rsm.decode_step(t["q"], t["k"], t["z"], t["v"], torch.from_numpy(s["f"]).cuda(), H, K,
+                                 want_idx=True)
+        torch.cuda.synchronize()
+        Hr = Hprev.cpu().numpy().astype(np.float64)
+        ro, ridx = oracle.decode_step(*(gen.as_f64(s[n], dtype) for n in "qkzv"), s["f"].astype(np.float64), Hr, K)
+        idx_n = idx.cpu().numpy()
+        assert np.array_equal(idx_n, ridx)
+        scale = float(np.max(np.abs(ro)))
+        check_close(o.cpu().numpy(), ro, scale, tol, f"decode o step {step}")
+        check_close(H.cpu().numpy(), Hr, scale, tol, f"decode H step {step}")
+        # rows not selected: bitwise unchanged
+        keep = np.ones((B, Hh, M), dtype=bool)
+        np.put_along_axis(keep, idx_n.astype(np.int64), False, axis=-1)
+        hn, hp = H.cpu().numpy(), Hprev.cpu().numpy()
+        assert np.array_equal(hn[keep].view(np.uint32), hp[keep].view(np.uint32))
+
+
+def test_prefill_then_decode_matches_longer_forward(rsm):
+    log("prefill + decode == forward")
+    d = gen.make_inputs(2, 200, 4, 64, 128, "bf16", seed=12)
+    t = dev_inputs(d, "cuda")
+    K, T1 = 16, 150
+    o, H, _ = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=64)
+    _, Hs, _ = rsm.forward_chunked(*(t[n][:, :T1] for n in "qkzvf"), K, C=64)
+    Hs = Hs.contiguous()
+    outs = []
+    for tt in range(T1, 200):
+        od, _ = rsm.decode_step(*(t[n][:, tt] for n in "qkzvf"), Hs, K)
+        outs.append(od)
+    torch.cuda.synchronize()
+    scale = float(o.abs().max())
+    check_close(torch.stack(outs, 1).cpu().numpy(), o[:, T1:].cpu().numpy().astype(np.float64), scale,
+                TOL["bf16"], "decode vs forward o")
+    check_close(Hs.cpu().numpy(), H.cpu().numpy().astype(np.float64), scale, TOL["bf16"], "decode vs forward H")
+
+
+def test_decode_workload_prefill_and_steps(rsm):
+    """Batched decode: 256 sequences x 16 heads, M64 Dv128 K16; prefill T=512 by the
+    chunked forward, then single-token steps.  The oracle follows sampled sequences from
+    its own float64 prefill (end to end) and from the GPU's fp32 state (decode alone)."""
+    log("decode workload: prefill")
+    w = gen.WORKLOADS["decode_b256"]
+    d = gen.make_workload("decode_b256")
+    t = dev_inputs(d, "cuda")
+    K = w.K
+    o, H, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=w.C, want_idx=True)
+    torch.cuda.synchronize()
+    samp = np.array([0, 37, 128, 255])
+    r = f64_inputs(d, samp)
+    ro, rH, ridx = oracle.forward(r["q"], r["k"], r["z"], r["v"], r["f"], K)
+    assert np.array_equal(idx.cpu().numpy()[samp], ridx)
+    scale = float(np.max(np.abs(ro)))
+    check_close(o.cpu().numpy()[samp], ro, scale, TOL["bf16"], "prefill o")
+    check_close(H.cpu().numpy()[samp], rH, scale, TOL["bf16"], "prefill H")
+    rng = np.random.default_rng(1000 + w.seed)
+    Hgpu_from = H.cpu().numpy()[samp].astype(np.float64)
+    for step in range(16):
+        s = gen.decode_step_inputs(rng, w.B, w.Hh, w.M, w.Dv, "bf16")
+        st = {n: to_torch(s[n], "bf16", "cuda") for n in "qkzv"}
+        od, idd = rsm.decode_step(st["q"], st["k"], st["z"], st["v"], torch.from_numpy(s["f"]).cuda(), H, K,
+                                  want_idx=True)
+        torch.cuda.synchronize()
+        args = [gen.as_f64(s[n][samp], "bf16") for n in "qkzv"] + [s["f"][samp].astype(np.float64)]
+        o_e2e, i_e2e = oracle.decode_step(*args, rH, K)
+        o_dec, _ = oracle.decode_step(*args, Hgpu_from, K)
+        assert np.array_equal(idd.cpu().numpy()[samp], i_e2e)
+        sc = float(np.max(np.abs(o_e2e)))
+        check_close(od.cpu().numpy()[samp], o_e2e, sc, TOL["bf16"], f"decode e2e step {step}")
+        check_close(od.cpu().numpy()[samp], o_dec, sc, TOL["bf16"], f"decode-only step {step}")
+        Hgpu_from = H.cpu().numpy()[samp].astype(np.float64)
