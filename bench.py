@@ -91,7 +91,7 @@ def main():
     sets = [to_dev(d, torch) for d in host_sets]
     o = torch.empty((w.B, w.T, w.Hh, w.Dv), dtype=torch.float32, device="cuda")
     Hs = torch.empty((w.B, w.Hh, w.M, w.Dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(rsm.forward_workspace_bytes(torch.bfloat16, w.B, w.T, w.Hh, w.M, w.Dv, w.C),
+    ws = torch.empty(rsm.forward_workspace_bytes(torch.bfloat16, w.B, w.T, w.Hh, w.M, w.Dv, w.C, w.K),
                      dtype=torch.uint8, device="cuda")
 
     def fwd(i):

@@ -77,11 +77,12 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
 
 /*
  * Bytes of device workspace rsm_forward_chunked needs for these sizes (0 if T == 0).
- * Returns 0 and leaves nothing to allocate for unsupported shapes as well; the
- * forward call then reports the shape error.
+ * The workspace holds the compact route of every token-head (the K selected slots and
+ * their decay factors), 5*K bytes per token-head plus padding to whole chunks.
+ * Returns 0 for unsupported arguments as well; the forward call then reports the error.
  */
 size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
-                                   int64_t Dv, int64_t C);
+                                   int64_t Dv, int64_t C, int64_t K);
 
 /*
  * Chunked forward over a whole sequence (RSM update and read of "How Raven Works",
@@ -94,7 +95,7 @@ size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, 
  *   H_out    [B,Hh,M,Dv]  fp32 out final state, or NULL; may be the same buffer as H0
  *   idx_out  [B,T,Hh,K]   int32 out selected slots (ascending), or NULL
  *   workspace/workspace_bytes: device scratch of at least
- *            rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C) bytes (owned by the
+ *            rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C, K) bytes (owned by the
  *            caller, contents undefined on entry and on return)
  * Slots never selected in the sequence come back in H_out bit-identical to H0.
  */

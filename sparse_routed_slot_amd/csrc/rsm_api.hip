@@ -74,10 +74,11 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
 }
 
 size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t Dv,
-                                   int64_t C) {
+                                   int64_t C, int64_t K) {
     if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv) || !c_ok(C)) return 0;
-    if (mul_ck({B, T, Hh, M}) < 0) return 0;
-    return rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C)).total;
+    if (K < 1 || K > M) return 0;
+    if (mul_ck({B, T + C, Hh, M, 5}) < 0) return 0;
+    return rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C), int(K)).total;
 }
 
 int rsm_forward_chunked(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
@@ -95,7 +96,7 @@ int rsm_forward_chunked(const void* q, const void* k, const void* z, const void*
     if (heads == 0) return RSM_OK;
     if (T > 0 && (!q || !k || !z || !v || !f || !o)) return RSM_ERR_NULL;
     const size_t es = esize(dtype);
-    const size_t need = rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C);
+    const size_t need = rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C, K);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RSM_ERR_WORKSPACE;
     const Range rq{q, size_t(rows * M) * es}, rk{k, size_t(rows * M) * es}, rz{z, size_t(rows * M) * es},
         rv{v, size_t(rows * Dv) * es}, rf{f, size_t(rows) * 4}, rh0{H0, size_t(heads * M * Dv) * 4},

@@ -102,7 +102,69 @@ __device__ __forceinline__ void wave_compact(const bool (&sel)[SPL], int (&pos)[
     }
 }
 
-__device__ __forceinline__ float sigmoidf_dev(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf_dev(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// ------------------------------------------------------------------------------------
+// Lane-per-row exact top-K: one lane owns one row of M logits in registers.
+//
+// Each logit becomes a packed key (order key of the value, then the inverted slot index)
+// so that all M packed keys of a row are distinct and ranking them descending ranks the
+// slots by (value descending, slot ascending) -- the top-K rule with ties to the lower
+// index.  A bitonic network sorts the packed keys descending; the K-th one is the
+// threshold, and slot i is selected iff its packed key >= the threshold.
+// bf16 inputs pack into 32 bits (16-bit key, 16-bit slot), fp32 inputs into 64 bits.
+// ------------------------------------------------------------------------------------
+template <typename T> struct RowKey;
+template <> struct RowKey<bf16_t> {
+    typedef uint32_t type;
+    __device__ static __forceinline__ type make(float x, int slot) {
+        return (order_key<16>(x) << 16) | uint32_t(0xFFFF - slot);
+    }
+};
+template <> struct RowKey<float> {
+    typedef unsigned long long type;
+    __device__ static __forceinline__ type make(float x, int slot) {
+        return ((unsigned long long)order_key<32>(x) << 32) | (unsigned long long)(0xFFFFFFFFu - uint32_t(slot));
+    }
+};
+
+template <typename U, int N>
+__device__ __forceinline__ void bitonic_sort_desc(U (&kv)[N]) {
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const U a = kv[i], b = kv[l];
+                    const U hi = a > b ? a : b, lo = a > b ? b : a;
+                    if ((i & k) == 0) {
+                        kv[i] = hi;
+                        kv[l] = lo;
+                    } else {
+                        kv[i] = lo;
+                        kv[l] = hi;
+                    }
+                }
+            }
+}
+
+// Threshold packed key of a row: the K-th largest of its M packed keys (K uniform).
+template <typename T, int M>
+__device__ __forceinline__ typename RowKey<T>::type row_threshold(const float (&x)[M], int K) {
+    typedef typename RowKey<T>::type U;
+    U kv[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) kv[i] = RowKey<T>::make(x[i], i);
+    bitonic_sort_desc<U, M>(kv);
+    U th = ~U(0);
+#pragma unroll
+    for (int r = 0; r < M; ++r) th = (r < K && kv[r] < th) ? kv[r] : th;
+    return th;
+}
+
 
 // MFMA fragment types (16x16 output tiles).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

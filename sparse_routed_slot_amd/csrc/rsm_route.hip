@@ -1,60 +1,148 @@
-// rsm_route.hip -- standalone router: sigmoid scores and exact top-K per token-head row.
+// rsm_route.hip -- router kernels: sigmoid scores and exact top-K per token-head row.
 //
-// RSM router of Raven (README page, "How Raven Works": TopK(sigmoid(r_proj(x)))), taking
-// the projected logits z as input.  One wave64 per row; slot r*64 + lane lives in lane
-// `lane`, register r.  The selection is computed on the order-preserving key of z, so
-// it equals ranking the exact sigmoid with ties to the lower slot index.
+// RSM router of Raven (README page, "How Raven Works": TopK(sigmoid(r_proj(x))) and
+// decay = exp(route_scores * f)), taking the projected logits z as input.
+//
+// One lane owns one row (M logits in registers); rows are contiguous in memory, so the
+// wave reads 64 consecutive rows.  The exact top-K with ties to the lower slot index comes
+// from a bitonic sort of distinct packed keys (rsm_device.h).  Selected slots are
+// collected in ascending slot order through per-lane LDS lists, then scored:
+//  * public router: idx (int32) and score = sigmoid(z) per selected slot;
+//  * forward router: the compact per-token route the chunked forward consumes -- slot
+//    (uint8) and alpha = exp(s*f) (fp32, exact: 0 for f = -inf, 1 when s*f == 0) -- in
+//    (batch*head, token) order, plus the optional int32 idx output in (b, t, h) order.
 #include "rsm_device.h"
 #include "rsm_launch.h"
 
 namespace rsm {
 
-template <typename T, int SPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const T* __restrict__ z, long n_rows, int M,
-                                                         int K, int32_t* __restrict__ idx,
-                                                         float* __restrict__ score) {
-    constexpr int NB = Elem<T>::kKeyBits;
-    const int lane = lane_id();
-    const long row = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= n_rows) return;  // whole wave leaves together
-    const T* zr = z + row * M;
-    uint32_t key[SPL];
-    float zv[SPL];
+// Raw row of M inputs held as 32-bit registers (two bf16 or one fp32 per register).
+template <typename T, int M> struct RowRegs;
+template <int M> struct RowRegs<bf16_t, M> {
+    static constexpr int NR = M / 2;
+    uint32_t r[NR];
+    __device__ __forceinline__ void load(const bf16_t* p) {
 #pragma unroll
-    for (int r = 0; r < SPL; ++r) {
-        const int slot = r * kWave + lane;
-        zv[r] = slot < M ? Elem<T>::load(zr, slot) : 0.0f;
-        key[r] = slot < M ? order_key<NB>(zv[r]) : 0u;
+        for (int v = 0; v < M / 8; ++v) {
+            const uint4 x = reinterpret_cast<const uint4*>(p)[v];
+            r[4 * v + 0] = x.x;
+            r[4 * v + 1] = x.y;
+            r[4 * v + 2] = x.z;
+            r[4 * v + 3] = x.w;
+        }
     }
-    bool sel[SPL];
-    wave_topk<SPL, NB>(key, K, sel);
-    int pos[SPL];
-    wave_compact<SPL>(sel, pos);
+    __device__ __forceinline__ float val(int i) const {
+        return __uint_as_float((i & 1) ? (r[i >> 1] & 0xFFFF0000u) : (r[i >> 1] << 16));
+    }
+};
+template <int M> struct RowRegs<float, M> {
+    float r[M];
+    __device__ __forceinline__ void load(const float* p) {
 #pragma unroll
-    for (int r = 0; r < SPL; ++r) {
-        if (sel[r]) {
-            idx[row * K + pos[r]] = r * kWave + lane;
-            if (score) score[row * K + pos[r]] = 1.0f / (1.0f + expf(-zv[r]));
+        for (int v = 0; v < M / 4; ++v) {
+            const float4 x = reinterpret_cast<const float4*>(p)[v];
+            r[4 * v + 0] = x.x;
+            r[4 * v + 1] = x.y;
+            r[4 * v + 2] = x.z;
+            r[4 * v + 3] = x.w;
+        }
+    }
+    __device__ __forceinline__ float val(int i) const { return r[i]; }
+};
+
+// kFwd = false: public router (idx int32 [row][K], score [row][K] or NULL).
+// kFwd = true : forward router (ridx uint8 / ralpha fp32 at [(b*Hh + h)*T_pad + t][K],
+//               idx int32 [row][K] or NULL).
+template <typename T, int M, bool kFwd>
+__global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z, const float* __restrict__ f,
+                                                        long n_rows, long T_len, int Hh, long T_pad, int K,
+                                                        int32_t* __restrict__ idx, float* __restrict__ score,
+                                                        uint8_t* __restrict__ ridx, float* __restrict__ ralpha) {
+    typedef typename RowKey<T>::type U;
+    extern __shared__ __align__(16) unsigned char smem[];
+    int* s_slot = reinterpret_cast<int*>(smem);              // [K][64]
+    float* s_val = reinterpret_cast<float*>(smem) + K * 64;  // [K][64]
+    const int lane = threadIdx.x;
+    const long row = long(blockIdx.x) * 64 + lane;
+    if (row >= n_rows) return;  // no cross-lane operations below
+
+    RowRegs<T, M> x;
+    x.load(z + row * M);
+    const bool dense = (K == M);
+    if (!dense) {
+        float v[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) v[i] = x.val(i);
+        const U th = row_threshold<T, M>(v, K);
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (RowKey<T>::make(v[i], i) >= th) {
+                s_slot[n * 64 + lane] = i;
+                s_val[n * 64 + lane] = v[i];
+                ++n;
+            }
+        }
+    }
+    long dst = row * K;
+    float ft = 0.0f;
+    if (kFwd) {
+        const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
+        dst = ((b * Hh + h) * T_pad + t) * K;
+        ft = f[row];
+    }
+    for (int n = 0; n < K; ++n) {
+        const int i = dense ? n : s_slot[n * 64 + lane];
+        const float zi = dense ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane];
+        const float s = sigmoidf_dev(zi);
+        if (kFwd) {
+            ridx[dst + n] = uint8_t(i);
+            ralpha[dst + n] = s > 0.0f ? __expf(s * ft) : 1.0f;
+            if (idx) idx[row * K + n] = i;
+        } else {
+            idx[dst + n] = i;
+            if (score) score[dst + n] = s;
         }
     }
 }
 
-template <typename T>
-static int launch_route(const T* z, long n_rows, int M, int K, int32_t* idx, float* score,
-                        hipStream_t stream) {
+template <typename T, bool kFwd>
+static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K,
+                       int32_t* idx, float* score, uint8_t* ridx, float* ralpha, hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
-    const dim3 grid(unsigned((n_rows + 3) / 4)), block(256);
-    if (M <= 64)
-        hipLaunchKernelGGL((route_topk_kernel<T, 1>), grid, block, 0, stream, z, n_rows, M, K, idx, score);
-    else
-        hipLaunchKernelGGL((route_topk_kernel<T, 2>), grid, block, 0, stream, z, n_rows, M, K, idx, score);
+    const dim3 grid(unsigned((n_rows + 63) / 64)), block(64);
+    const size_t lds = size_t(K) * 64 * 8;
+#define RSM_ROUTE_LAUNCH(MM)                                                                                    \
+    hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, T_pad, \
+                       K, idx, score, ridx, ralpha)
+    switch (M) {
+        case 16: RSM_ROUTE_LAUNCH(16); break;
+        case 32: RSM_ROUTE_LAUNCH(32); break;
+        case 64: RSM_ROUTE_LAUNCH(64); break;
+        case 128: RSM_ROUTE_LAUNCH(128); break;
+        default: return RSM_ERR_UNSUPPORTED;
+    }
+#undef RSM_ROUTE_LAUNCH
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx, float* score,
                       hipStream_t stream) {
-    if (dtype == RSM_F32) return launch_route(static_cast<const float*>(z), n_rows, M, K, idx, score, stream);
-    return launch_route(static_cast<const bf16_t*>(z), n_rows, M, K, idx, score, stream);
+    if (dtype == RSM_F32)
+        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+                                         nullptr, nullptr, stream);
+    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+                                      nullptr, nullptr, stream);
+}
+
+int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
+                     int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream) {
+    const long n_rows = B * T * Hh;
+    if (dtype == RSM_F32)
+        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+                                        nullptr, ridx, ralpha, stream);
+    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+                                     nullptr, ridx, ralpha, stream);
 }
 
 }  // namespace rsm

@@ -45,7 +45,7 @@ def load():
     lib.rsm_abi_version.restype = I
     lib.rsm_route_topk.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P]
     lib.rsm_route_topk.restype = I
-    lib.rsm_forward_workspace_bytes.argtypes = [I, I64, I64, I64, I64, I64, I64]
+    lib.rsm_forward_workspace_bytes.argtypes = [I, I64, I64, I64, I64, I64, I64, I64]
     lib.rsm_forward_workspace_bytes.restype = ctypes.c_size_t
     lib.rsm_forward_chunked.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P,
                                         ctypes.c_size_t, P]
@@ -95,8 +95,8 @@ def route_topk(z: torch.Tensor, K: int, want_score: bool = True) -> Tuple[torch.
     return idx, score
 
 
-def forward_workspace_bytes(dtype: torch.dtype, B: int, T: int, Hh: int, M: int, Dv: int, C: int) -> int:
-    return int(load().rsm_forward_workspace_bytes(DTYPE_CODES[dtype], B, T, Hh, M, Dv, C))
+def forward_workspace_bytes(dtype: torch.dtype, B: int, T: int, Hh: int, M: int, Dv: int, C: int, K: int) -> int:
+    return int(load().rsm_forward_workspace_bytes(DTYPE_CODES[dtype], B, T, Hh, M, Dv, C, K))
 
 
 def forward_chunked(q, k, z, v, f, K: int, C: int = 64, H0: Optional[torch.Tensor] = None,
@@ -122,7 +122,7 @@ def forward_chunked(q, k, z, v, f, K: int, C: int = 64, H0: Optional[torch.Tenso
     if want_state:
         H = state_out if state_out is not None else torch.empty((B, Hh, M, Dv), dtype=torch.float32, device=dev)
     idx = torch.empty((B, T, Hh, K), dtype=torch.int32, device=dev) if want_idx else None
-    need = forward_workspace_bytes(q.dtype, B, T, Hh, M, Dv, C)
+    need = forward_workspace_bytes(q.dtype, B, T, Hh, M, Dv, C, K)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(load().rsm_forward_chunked(

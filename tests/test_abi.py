@@ -24,7 +24,7 @@ def lib():
     L = ctypes.CDLL(LIB)
     L.rsm_status_string.restype = ctypes.c_char_p
     L.rsm_route_topk.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, I64, P, P, P]
-    L.rsm_forward_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, I64]
+    L.rsm_forward_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64, I64, I64, I64, I64]
     L.rsm_forward_workspace_bytes.restype = ctypes.c_size_t
     L.rsm_forward_chunked.argtypes = [P, P, P, P, ctypes.c_int, P, P, I64, I64, I64, I64, I64, I64, I64,
                                       P, P, P, P, ctypes.c_size_t, P]
@@ -95,14 +95,15 @@ def test_forward_argument_errors(lib):
 
 def test_workspace_size(lib):
     f = lib.rsm_forward_workspace_bytes
-    assert f(1, 8, 2048, 8, 64, 128, 64) > 0
-    assert f(1, 8, 0, 8, 64, 128, 64) == 0
-    assert f(1, 8, 2048, 8, 48, 128, 64) == 0          # unsupported M
-    # grows with T and with the element size
-    assert f(1, 1, 4096, 8, 64, 128, 64) > f(1, 1, 2048, 8, 64, 128, 64)
-    assert f(0, 1, 2048, 8, 64, 128, 64) > f(1, 1, 2048, 8, 64, 128, 64)
-    # at least the per-chunk tiles: 2 * C * M elements per (b, h, chunk)
-    assert f(1, 2, 128, 4, 64, 128, 64) >= 2 * 4 * 2 * (2 * 64 * 64 * 2)
+    assert f(1, 8, 2048, 8, 64, 128, 64, 16) > 0
+    assert f(1, 8, 0, 8, 64, 128, 64, 16) == 0
+    assert f(1, 8, 2048, 8, 48, 128, 64, 16) == 0      # unsupported M
+    assert f(1, 8, 2048, 8, 64, 128, 64, 65) == 0      # K > M
+    # the compact route: K slots (1 byte) and K decay factors (4 bytes) per padded token-head
+    assert f(1, 8, 2048, 8, 64, 128, 64, 16) >= 8 * 2048 * 8 * 16 * 5
+    assert f(1, 1, 100, 2, 64, 128, 64, 16) >= 1 * 128 * 2 * 16 * 5   # T padded to whole chunks
+    assert f(1, 1, 4096, 8, 64, 128, 64, 16) > f(1, 1, 2048, 8, 64, 128, 64, 16)
+    assert f(0, 1, 2048, 8, 64, 128, 64, 16) == f(1, 1, 2048, 8, 64, 128, 64, 16)
 
 
 def dec(lib, dtype=1, B=4, Hh=2, M=64, Dv=128, K=8, H=F_, o=G_, idx=None, q=A):
