@@ -17,18 +17,21 @@
 //
 // Kernels:
 //  * route (rsm_route.hip, fully parallel): exact top-K per token-head and alpha, written as
-//    a compact list (slot, alpha) per token -- the only intermediate in memory.
+//    a compact list (slot, alpha) per token, or as dense alphas when K is a large fraction
+//    of M -- the only intermediate in memory.
 //  * fwd_scan (one workgroup per (batch, head, Dv tile)): walks the chunks in order with the
-//    fp32 state tile in registers.  Per chunk it scatters the alphas into a dense tile in
-//    LDS, forms the decay products E by prefix products along the chunk, builds Qh and Kh
-//    in LDS, runs the three contractions on 16x16 MFMA tiles, writes o, and updates the
-//    state.  Rows of slots untouched in a chunk (E_last == 1) are not written, so they keep
-//    their exact bits.  The next chunk's inputs are loaded into registers while the current
-//    chunk computes.
+//    fp32 state tile in registers.  The chunk's raw q, k, v tiles and its route arrive in
+//    LDS by direct global->LDS loads issued while the previous chunk computes.  Per chunk it
+//    scatters the alphas into a dense tile in LDS, forms the decay products E by prefix
+//    products along the chunk, builds Qh and Kh in LDS, runs the three contractions on
+//    16x16 MFMA tiles, writes o, and updates the state.  Rows of slots untouched in a chunk
+//    (E_last == 1) are not written, so they keep their exact bits.
 //
 // Overflow guard: 1/E grows with the decay accumulated in a chunk.  On the factored path each
 // alpha is clamped below at e^-30 (~1e-13 instead of 0); a chunk whose decay product falls
 // below 2^-100 for some slot is evaluated token by token with the exact alphas instead.
+#include <type_traits>
+
 #include "rsm_device.h"
 #include "rsm_launch.h"
 
@@ -36,6 +39,12 @@ namespace rsm {
 
 constexpr float kAlphaMin = 9.3576230e-14f;  // e^-30: clamp of alpha on the factored path
 constexpr float kSafeMin = 7.8886091e-31f;   // 2^-100: smallest E_last kept factored
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 // ------------------------------------------------------------------------------------
 // Operand policy.  16x16 MFMA output tiles; a k-block of KB along the contraction with
@@ -48,10 +57,18 @@ constexpr float kSafeMin = 7.8886091e-31f;   // 2^-100: smallest E_last kept fac
 // operands takes three MFMAs (hi*hi + hi*lo + lo*hi); V times a derived operand takes two.
 // A single bf16 rounding of a derived operand costs up to 2^-9 of |o| wherever one term
 // dominates an output -- the whole bf16 error budget.
+//
+// Contractions over chunk rows j use the k-slot order j = jperm(kb, q4, e), the row order in
+// which the S^T accumulator tiles hold P^T (rows 16*J + 4*q4 + r).  Contractions over slots
+// use the natural order i = KB*kb + EPL*q4 + e.  A "column" fragment (k along the rows of a
+// row-major LDS array) is gathered with ds_read_b64_tr_b16 for bf16: within each 16-lane
+// group, lane 4a+b receives element b of the 8-byte blocks addressed by lanes a, a+4, a+8,
+// a+12; so lane (a + 4e) addresses row rho(e), columns 4a..4a+3.
 // ------------------------------------------------------------------------------------
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
+//
+// Every LDS access is written as one offset from its array (arr + off): the compiler then
+// keeps track of which array each access touches and does not make it wait for the direct
+// global->LDS loads still in flight into other arrays.
 template <typename T> struct Pol;
 
 template <> struct Pol<float> {
@@ -61,21 +78,24 @@ template <> struct Pol<float> {
     struct dfrag {
         frag p[1];
     };
-    __device__ static __forceinline__ frag ld(const E* p) { return *p; }
-    // k-slot f = kb*EPL + e of a contraction over chunk rows j <-> j = 16(f/4) + 4*q4 + f%4
     __device__ static __forceinline__ int jperm(int kb, int q4, int e) { return 16 * (kb >> 2) + 4 * q4 + (kb & 3); }
-    __device__ static __forceinline__ frag ld_perm(const E* row, int kb, int q4) { return row[jperm(kb, q4, 0)]; }
-    __device__ static __forceinline__ frag ld_perm_strided(const E* col, int stride, int kb, int q4) {
-        return col[jperm(kb, q4, 0) * stride];
+    __device__ static __forceinline__ int inat(int kb, int q4, int e) { return 4 * kb + q4; }
+    __device__ static __forceinline__ frag ld(const E* arr, int off) { return arr[off]; }
+    // column fragment: rows rho(kb, q4, e) of a row-major array with `pitch`, columns from
+    // element offset off0 (plane + first column)
+    template <bool PERM>
+    __device__ static __forceinline__ frag ld_col(const E* arr, int off0, int pitch, int kb, int q4, int l16) {
+        const int row = PERM ? jperm(kb, q4, 0) : inat(kb, q4, 0);
+        return arr[off0 + row * pitch + l16];
     }
-    __device__ static __forceinline__ void put(E* base, int ps, int i, float x) { base[i] = x; }
-    __device__ static __forceinline__ void put_pair(E* base, int ps, int i0, int i1, float a, float b) {
-        base[i0] = a;
-        base[i1] = b;
+    __device__ static __forceinline__ void put(E* arr, int ps, int i, float x) { arr[i] = x; }
+    // 4 consecutive values (16-byte aligned)
+    __device__ static __forceinline__ void put4(E* arr, int ps, int i, float a, float b, float c, float d) {
+        *reinterpret_cast<float4*>(arr + i) = make_float4(a, b, c, d);
     }
-    // EVT = 4 consecutive values at base[i] (16-byte aligned)
-    __device__ static __forceinline__ void put_vec(E* base, int ps, int i, const float* x) {
-        *reinterpret_cast<float4*>(base + i) = make_float4(x[0], x[1], x[2], x[3]);
+    // EVT = 4 consecutive values (16-byte aligned)
+    __device__ static __forceinline__ void put_vec(E* arr, int ps, int i, const float* x) {
+        *reinterpret_cast<float4*>(arr + i) = make_float4(x[0], x[1], x[2], x[3]);
     }
     template <int NT>
     __device__ static __forceinline__ dfrag pack_perm(const floatx4 (&st)[NT], int kb) {
@@ -97,27 +117,22 @@ template <> struct Pol<bf16_t> {
     struct dfrag {
         frag p[2];  // hi, lo
     };
-    __device__ static __forceinline__ frag ld(const E* p) {
-        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
-    }
     __device__ static __forceinline__ int jperm(int kb, int q4, int e) {
         return 32 * kb + 16 * (e >> 2) + 4 * q4 + (e & 3);
     }
-    // two runs of four consecutive j
-    __device__ static __forceinline__ frag ld_perm(const E* row, int kb, int q4) {
-        const uint2 a = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * q4);
-        const uint2 b = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * q4);
-        return __builtin_bit_cast(frag, make_uint4(a.x, a.y, b.x, b.y));
+    __device__ static __forceinline__ int inat(int kb, int q4, int e) { return 32 * kb + 8 * q4 + e; }
+    __device__ static __forceinline__ frag ld(const E* arr, int off) {
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(arr + off));
     }
-    __device__ static __forceinline__ frag ld_perm_strided(const E* col, int stride, int kb, int q4) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t lo = col[jperm(kb, q4, 2 * p) * stride].bits;
-            const uint32_t hi = col[jperm(kb, q4, 2 * p + 1) * stride].bits;
-            w[p] = lo | (hi << 16);
-        }
-        return __builtin_bit_cast(frag, make_uint4(w[0], w[1], w[2], w[3]));
+    template <bool PERM>
+    __device__ static __forceinline__ frag ld_col(const E* arr, int off0, int pitch, int kb, int q4, int l16) {
+        const int er = l16 >> 2, c4 = 4 * (l16 & 3);
+        const int r0 = PERM ? jperm(kb, q4, er) : inat(kb, q4, er);
+        const int r1 = PERM ? jperm(kb, q4, 4 + er) : inat(kb, q4, 4 + er);
+        const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (off0 + r0 * pitch + c4)));
+        const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (off0 + r1 * pitch + c4)));
+        const uint2 xa = __builtin_bit_cast(uint2, x), ya = __builtin_bit_cast(uint2, y);
+        return __builtin_bit_cast(frag, make_uint4(xa.x, xa.y, ya.x, ya.y));
     }
     __device__ static __forceinline__ uint32_t split2(float a, float b, uint32_t& lo) {
         const floatx2 x = {a, b};
@@ -126,27 +141,24 @@ template <> struct Pol<bf16_t> {
         lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
         return __builtin_bit_cast(uint32_t, hi);
     }
-    __device__ static __forceinline__ void put(E* base, int ps, int i, float x) {
+    __device__ static __forceinline__ void put(E* arr, int ps, int i, float x) {
         uint32_t lo;
         const uint32_t hi = split2(x, 0.0f, lo);
-        base[i].bits = uint16_t(hi);
-        base[ps + i].bits = uint16_t(lo);
+        arr[i].bits = uint16_t(hi);
+        arr[ps + i].bits = uint16_t(lo);
     }
-    __device__ static __forceinline__ void put_pair(E* base, int ps, int i0, int i1, float a, float b) {
-        uint32_t lo;
-        const uint32_t hi = split2(a, b, lo);
-        base[i0].bits = uint16_t(hi);
-        base[i1].bits = uint16_t(hi >> 16);
-        base[ps + i0].bits = uint16_t(lo);
-        base[ps + i1].bits = uint16_t(lo >> 16);
+    __device__ static __forceinline__ void put4(E* arr, int ps, int i, float a, float b, float c, float d) {
+        uint32_t l0, l1;
+        const uint32_t h0 = split2(a, b, l0), h1 = split2(c, d, l1);
+        *reinterpret_cast<uint2*>(arr + i) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(arr + (ps + i)) = make_uint2(l0, l1);
     }
-    // EVT = 8 consecutive values at base[i] (16-byte aligned): one 16-byte store per plane
-    __device__ static __forceinline__ void put_vec(E* base, int ps, int i, const float* x) {
+    __device__ static __forceinline__ void put_vec(E* arr, int ps, int i, const float* x) {
         uint32_t l0, l1, l2, l3;
         const uint32_t h0 = split2(x[0], x[1], l0), h1 = split2(x[2], x[3], l1);
         const uint32_t h2 = split2(x[4], x[5], l2), h3 = split2(x[6], x[7], l3);
-        *reinterpret_cast<uint4*>(base + i) = make_uint4(h0, h1, h2, h3);
-        *reinterpret_cast<uint4*>(base + ps + i) = make_uint4(l0, l1, l2, l3);
+        *reinterpret_cast<uint4*>(arr + i) = make_uint4(h0, h1, h2, h3);
+        *reinterpret_cast<uint4*>(arr + (ps + i)) = make_uint4(l0, l1, l2, l3);
     }
     template <int NT>
     __device__ static __forceinline__ dfrag pack_perm(const floatx4 (&st)[NT], int kb) {
@@ -189,85 +201,91 @@ __device__ __forceinline__ void unpack16(const uint4& x, float (&v)[8], float) {
     v[3] = __uint_as_float(x.w);
 }
 
-// LDS plan of the scan kernel (byte offsets).  Row pitches padded by one 16-byte vector.
-template <typename T, int M, int C, int DT>
-struct ScanCfg {
-    typedef Pol<T> P;
-    typedef typename P::E E;
-    static constexpr int KB = P::KB, NPL = P::NPL;
-    static constexpr int MP = M > KB ? M : KB;  // padded slot dimension
-    static constexpr int CP = C > KB ? C : KB;  // padded chunk dimension
-    static constexpr int EVE = 16 / int(sizeof(E));
-    static constexpr int EVT = 16 / int(sizeof(T));
-    static constexpr int QP = MP + EVE;      // pitch of sQ, sK, sHt rows
-    static constexpr int TP = CP + EVT;      // pitch of sVt rows
-    static constexpr int NPART = 256 / M;    // token parts of the prefix product
-    static constexpr int TPP = C / NPART;    // tokens per part
-    static constexpr int psQ = C * QP;       // plane sizes (elements)
-    static constexpr int psHt = DT * QP;
-    static constexpr int szQ = NPL * psQ * int(sizeof(E));
-    static constexpr int szX = (M * DT * 4 + C * M + 15) / 16 * 16;     // exact-path scratch
-    static constexpr int offQ = 0;
-    static constexpr int offK = szQ;
-    static constexpr int offA = 2 * szQ > szX ? 2 * szQ : szX;           // float [C][M]
-    static constexpr int offKr = offA + C * M * 4;                        // T [C][M]
-    static constexpr int offVt = offKr + C * M * int(sizeof(T));          // T [DT][TP]
-    static constexpr int offHt = offVt + DT * TP * int(sizeof(T));        // E planes [DT][QP]
-    static constexpr int offTot = offHt + NPL * psHt * int(sizeof(E));    // float [NPART][M]
-    static constexpr int offE = offTot + NPART * M * 4;                   // float [M]
-    static constexpr int total = (offE + M * 4 + 15) / 16 * 16;
-    // exact-path scratch: state [M][DT] fp32 and slots [C][K] (uint8) inside sQ/sK; the exact
-    // alphas [C][K] go to sA
-    static constexpr int offHf = 0;
-    static constexpr int offRa = M * DT * 4;
-    static_assert(offRa + C * M <= offA, "exact-path scratch must fit below sA");
-};
-
-// floor(n / K) for 0 <= n < 2^20 from a float reciprocal, corrected to the exact quotient
-__device__ __forceinline__ int div_small(int n, int K, float invK) {
-    int qt = int(float(n) * invK);
-    qt -= (qt * K > n) ? 1 : 0;
-    qt += ((qt + 1) * K <= n) ? 1 : 0;
-    return qt;
+// f(i) for i = tid, tid + NT, ... below N, with a trip count known at compile time.
+template <int N, int NT, typename F>
+__device__ __forceinline__ void for_each_tid(int tid, F f) {
+#pragma unroll
+    for (int it = 0; it < (N + NT - 1) / NT; ++it) {
+        const int i = tid + NT * it;
+        if (N % NT == 0 || i < N) f(i);
+    }
 }
+
+// Direct global->LDS copy of a chunk tile: wave-instruction r moves LDS bytes
+// [r*1024, r*1024 + 1024) of `lds`, lane l the 16 bytes at r*1024 + 16*l, taken from the
+// global address src(byte offset).  `nbytes` is a multiple of 1024 (the LDS array is padded).
+template <int NW, typename F>
+__device__ __forceinline__ void dma_tile(void* lds, int nbytes, int w, int lane, F src) {
+    for (int r = w; r * 1024 < nbytes; r += NW) {
+        const void* g = src(r * 1024 + 16 * lane);
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(static_cast<unsigned char*>(lds) + r * 1024), 16, 0, 0);
+    }
+}
+
+constexpr int pad1k(int bytes) { return (bytes + 1023) / 1024 * 1024; }
+
+// Workgroup barrier without a memory fence.  A workgroup-scope release fence would also
+// wait for every direct global->LDS load still in flight; the scan waits for those
+// explicitly, one chunk later.  LDS is coherent inside the workgroup, so each wave's own
+// LDS accesses having completed (lgkmcnt = 0) before s_barrier is what makes them visible.
+// The signal fences keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Compact route capacity: K up to KC uses (slot, alpha) lists, larger K dense alphas.
+constexpr int compact_cap(int M) { return M / 2 < 32 ? M / 2 : 32; }
 
 // ------------------------------------------------------------------------------------
 // Scan: one workgroup (4 waves) per (b, h, Dv tile of DT columns); sequential over chunks.
+// DENSE: the route arrives as dense alphas [C][M] instead of (slot, alpha) lists.
 // ------------------------------------------------------------------------------------
-template <typename T, int M, int C, int DT>
+template <typename T, int M, int C, int DT, bool DENSE>
 __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
     long T_len, int Hh, int Dv, int K, long nC, const uint8_t* __restrict__ ridx, const float* __restrict__ ralpha,
     float* __restrict__ o, float* __restrict__ H_out) {
-    typedef ScanCfg<T, M, C, DT> Cfg;
-    typedef typename Cfg::P P;
+    typedef Pol<T> P;
     typedef typename P::E E;
     typedef typename P::frag frag;
     typedef typename P::dfrag dfrag;
+    constexpr int NW = 4, NT = 64 * NW;
     constexpr int KB = P::KB, EPL = P::EPL, NPL = P::NPL;
-    constexpr int MP = Cfg::MP, CP = Cfg::CP, QP = Cfg::QP, TP = Cfg::TP, EVT = Cfg::EVT;
-    constexpr int psQ = Cfg::psQ, psHt = Cfg::psHt;
+    constexpr int MP = M > KB ? M : KB;        // padded slot dimension (k of slot contractions)
+    constexpr int CP = C > KB ? C : KB;        // padded chunk dimension (k of row contractions)
+    constexpr int EVE = 16 / int(sizeof(E));   // elements per 16 bytes
+    constexpr int QP = MP + EVE;               // pitch of Qh / Kh rows
+    constexpr int HP = DT + EVE;               // pitch of state rows
     constexpr int NTC = C / 16, NTCP = CP / 16, NTD = DT / 16, NTM = M / 16;
-    constexpr int NIW = (NTM + 3) / 4;   // slot tiles owned per wave (I = w + 4*jI)
-    constexpr int UPW = NIW * NTD;       // state tiles per wave: (I, D) for D = 0..NTD-1
+    constexpr int NIW = (NTM + NW - 1) / NW;  // slot tiles per wave (I = w + NW*jI)
+    constexpr int UPW = NIW * NTD;             // state tiles per wave
     constexpr int NKM = MP / KB, NKC = CP / KB;
-    constexpr int NPART = Cfg::NPART, TPP = Cfg::TPP;
-    constexpr int NVQ = (C * M / EVT + 255) / 256;   // q / k tile vectors per thread
-    constexpr int NVV = (C * DT / EVT + 255) / 256;  // v tile vectors per thread
-    constexpr int MAXRA = (C * M / 4 + 255) / 256;   // route vectors (4 entries) per thread, K <= M
+    constexpr int NPART = NT / M, TPP = C / NPART;
+    constexpr int KC = compact_cap(M);
+    constexpr int EVT = 16 / int(sizeof(T));
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    E* sQ = reinterpret_cast<E*>(smem + Cfg::offQ);
-    E* sK = reinterpret_cast<E*>(smem + Cfg::offK);
-    float* sA = reinterpret_cast<float*>(smem + Cfg::offA);
-    T* sKr = reinterpret_cast<T*>(smem + Cfg::offKr);
-    T* sVt = reinterpret_cast<T*>(smem + Cfg::offVt);
-    E* sHt = reinterpret_cast<E*>(smem + Cfg::offHt);
-    float* sTot = reinterpret_cast<float*>(smem + Cfg::offTot);
-    float* sE = reinterpret_cast<float*>(smem + Cfg::offE);
-    float* sHf = reinterpret_cast<float*>(smem + Cfg::offHf);       // exact path: state [M][DT]
-    uint8_t* sRi = reinterpret_cast<uint8_t*>(smem + Cfg::offRa);   // exact path: slots [C][K]
-    float* sRa = sA;                                                // exact path: alphas [C][K]
+    // LDS.  Raw inputs land by direct loads (tile arrays padded to 1 KB); every array is a
+    // separate object so the compiler can tell the direct loads from the other accesses.
+    __shared__ __align__(16) T rq[pad1k(C * M * int(sizeof(T))) / int(sizeof(T))];
+    __shared__ __align__(16) T rk[pad1k(C * M * int(sizeof(T))) / int(sizeof(T))];
+    __shared__ __align__(16) T rv0[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, even chunks
+    __shared__ __align__(16) T rv1[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, odd chunks
+    __shared__ __align__(16) float rA[DENSE ? 4 : pad1k(C * KC * 4) / 4];
+    __shared__ __align__(16) uint8_t rI[DENSE ? 16 : pad1k(C * KC)];
+    __shared__ __align__(16) float sA[pad1k(C * M * 4) / 4];  // alphas -> decay products E
+    __shared__ __align__(16) E sQK[2 * NPL * (CP * QP + 8)];  // Qh planes, then Kh planes
+    __shared__ __align__(16) E sH[NPL * MP * HP];             // state copy, row-major [i][d]
+    __shared__ float sTot[NPART * M];
+    __shared__ float sE[M];
+    __shared__ int sFlag[NW];
+    constexpr int psQ = CP * QP + 8;                          // plane stride of Qh / Kh
+    constexpr int psH = MP * HP;                              // plane stride of the state copy
+    constexpr int oK = NPL * psQ;                             // Kh planes start here
+    float* sHf = reinterpret_cast<float*>(sQK);               // exact path: state [M][DT]
+    static_assert(M * DT * 4 <= int(sizeof(sQK)), "exact-path state must fit in the Qh/Kh area");
 
     // workgroup -> (head, Dv tile); the Dv tiles of one head land on the same XCD
     // (workgroups are dealt to the 8 XCDs round-robin) so they share inputs in its L2.
@@ -279,138 +297,130 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     const int d0 = int(id % nDT) * DT;
     const long h = bh % Hh, b = bh / Hh;
     const long T_pad = nC * C;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
-    const int nra = (C * K / 4 + 255) / 256;  // route vectors per thread (uniform)
-    const float invK = 1.0f / float(K);
-    const long tstride = long(Hh);            // rows between consecutive tokens of a head
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    // wave index in a scalar register: every branch on it is a uniform scalar branch (no
+    // EXEC masking around the MFMAs, which would not be skipped lane by lane)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // compact route entries: thread -> token rt, entries rsub, rsub + RPT, ... (< K)
+    constexpr int RPT = NT / C;
+    const int rt = tid / RPT, rsub = tid % RPT;
+    const long rstride = long(Hh);  // rows between consecutive tokens of one head
 
-    for (int i = tid * 16; i < Cfg::total; i += 256 * 16)
-        *reinterpret_cast<uint4*>(smem + i) = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    for (int i = tid; i < C * M; i += 256) sA[i] = 1.0f;
+    // ---- direct loads of chunk c's inputs (rows past the sequence end repeat the last row;
+    // their tokens carry no route entries, so they contribute nothing)
+    auto issue_qk = [&](long c) {
+        const int nv = int(T_len - c * C < C ? T_len - c * C : C);
+        const char* qb = reinterpret_cast<const char*>(q + ((b * T_len + c * C) * rstride + h) * M);
+        const char* kb_ = reinterpret_cast<const char*>(k + ((b * T_len + c * C) * rstride + h) * M);
+        constexpr int RB = M * int(sizeof(T));
+        auto fq = [&](int off) {
+            const int t = min(off / RB, nv - 1), cb = off % RB;
+            return static_cast<const void*>(qb + long(t) * rstride * RB + cb);
+        };
+        auto fk = [&](int off) {
+            const int t = min(off / RB, nv - 1), cb = off % RB;
+            return static_cast<const void*>(kb_ + long(t) * rstride * RB + cb);
+        };
+        dma_tile<NW>(rq, int(sizeof(rq)), w, lane, fq);
+        dma_tile<NW>(rk, int(sizeof(rk)), w, lane, fk);
+    };
+    auto issue_v = [&](long c, T* dst) {
+        const int nv = int(T_len - c * C < C ? T_len - c * C : C);
+        const char* vb = reinterpret_cast<const char*>(v + ((b * T_len + c * C) * rstride + h) * Dv + d0);
+        constexpr int RB = DT * int(sizeof(T));
+        const long gpitch = rstride * Dv * long(sizeof(T));
+        auto fv = [&](int off) {
+            const int t = min(off / RB, nv - 1), cb = off % RB;
+            return static_cast<const void*>(vb + t * gpitch + cb);
+        };
+        dma_tile<NW>(dst, int(sizeof(rv0)), w, lane, fv);
+    };
+    auto issue_route = [&](long c) {
+        if (DENSE) {
+            const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * M);
+            auto fa = [&](int off) { return static_cast<const void*>(ab + min(off, C * M * 4 - 16)); };
+            dma_tile<NW>(sA, int(sizeof(sA)), w, lane, fa);
+        } else {
+            const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * K);
+            const char* ib = reinterpret_cast<const char*>(ridx + (bh * T_pad + c * C) * K);
+            const int na = C * K * 4, ni = C * K;
+            auto fa = [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); };
+            auto fi = [&](int off) { return static_cast<const void*>(ib + min(off, ni - 16)); };
+            dma_tile<NW>(rA, pad1k(na), w, lane, fa);
+            dma_tile<NW>(rI, pad1k(ni), w, lane, fi);
+        }
+    };
 
-    // state tile j = jI*NTD + D holds H[i = 16*I + l16][d = 16*D + 4*q4 + r], I = w + 4*jI
+    // ---- initial state: registers (tile j = jI*NTD + D holds H[16*I + l16][16*D + 4*q4 + r]).
+    // Padding (slot rows past M, chunk rows past C when a k-block is longer) stays zero.
+    for (int i = tid; i < int(sizeof(sQK) / sizeof(E)); i += NT) sQK[i] = E{};
+    for (int i = tid; i < int(sizeof(sH) / sizeof(E)); i += NT) sH[i] = E{};
+    wg_barrier();
     floatx4 Hreg[UPW];
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-        const int I = w + 4 * (j / NTD), D = j % NTD, i = 16 * I + l16;
+        const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
         Hreg[j] = floatx4{0.f, 0.f, 0.f, 0.f};
         if (I < NTM) {
             if (H0) {
                 const float4 x = *reinterpret_cast<const float4*>(H0 + (bh * M + i) * Dv + d0 + 16 * D + 4 * q4);
                 Hreg[j] = floatx4{x.x, x.y, x.z, x.w};
             }
-            const int r0 = (16 * D + 4 * q4) * QP + i;
-            P::put_pair(sHt, psHt, r0, r0 + QP, Hreg[j][0], Hreg[j][1]);
-            P::put_pair(sHt, psHt, r0 + 2 * QP, r0 + 3 * QP, Hreg[j][2], Hreg[j][3]);
+            P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
         }
     }
-
-    // ---- register prefetch of one chunk's inputs
-    uint4 pq[NVQ], pk[NVQ], pv[NVV];
-    float4 pa[MAXRA];
-    uint32_t pi[MAXRA];
-    auto load_qk = [&](long c, uint4 (&dst)[NVQ], const T* src) {
-        const T* base = src + ((b * T_len + c * C) * tstride + h) * M;
-        const int nv = int(T_len - c * C < C ? T_len - c * C : C);
-#pragma unroll
-        for (int r = 0; r < NVQ; ++r) {
-            const int u = tid + 256 * r;
-            const int t = (u * EVT) / M, i0 = (u * EVT) % M;
-            dst[r] = make_uint4(0u, 0u, 0u, 0u);
-            if (u < C * M / EVT && t < nv) dst[r] = *reinterpret_cast<const uint4*>(base + t * tstride * M + i0);
-        }
-    };
-    auto load_v = [&](long c) {
-        const T* base = v + ((b * T_len + c * C) * tstride + h) * Dv + d0;
-        const int nv = int(T_len - c * C < C ? T_len - c * C : C);
-#pragma unroll
-        for (int r = 0; r < NVV; ++r) {
-            const int u = tid + 256 * r;
-            const int t = (u * EVT) / DT, c0 = (u * EVT) % DT;
-            pv[r] = make_uint4(0u, 0u, 0u, 0u);
-            if (u < C * DT / EVT && t < nv) pv[r] = *reinterpret_cast<const uint4*>(base + t * tstride * Dv + c0);
-        }
-    };
-    auto load_route = [&](long c) {
-        const long base = (bh * T_pad + c * C) * K;
-#pragma unroll
-        for (int r = 0; r < MAXRA; ++r) {
-            const int u = tid + 256 * r;
-            if (r < nra && u < C * K / 4) {
-                pa[r] = *reinterpret_cast<const float4*>(ralpha + base + 4 * u);
-                pi[r] = *reinterpret_cast<const uint32_t*>(ridx + base + 4 * u);
-            } else {
-                pa[r] = make_float4(1.f, 1.f, 1.f, 1.f);
-                pi[r] = 0u;
-            }
-        }
-    };
     if (nC > 0) {
-        load_qk(0, pq, q);
-        load_qk(0, pk, k);
-        load_v(0);
-        load_route(0);
+        issue_qk(0);
+        issue_v(0, rv0);
+        issue_route(0);
     }
+    if (!DENSE)
+        for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
 
-    for (long c = 0; c < nC; ++c) {
+    // One chunk.  CUR selects the v buffer statically (even chunks rv0, odd chunks rv1) so
+    // the compiler can tell the in-flight loads of the next chunk's v from this chunk's reads.
+    auto chunk = [&](auto cur, long c) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur)::value;
         const long tokc = c * C;
         const int nvalid = int(T_len - tokc < C ? T_len - tokc : C);
-        __syncthreads();  // previous chunk: every read of sQ, sK, sVt, sKr is done
+        const T* rvc = CUR ? rv1 : rv0;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
+        wg_barrier();                   // ... and every other wave's
+        if (c + 1 < nC) issue_v(c + 1, CUR ? rv0 : rv1);
 
-        // ---- stage raw k and V^T, scatter the clamped alphas, clear Kh
+        // ---- scatter the clamped alphas (compact route), clear Kh
+        if (!DENSE && rt < nvalid) {
 #pragma unroll
-        for (int r = 0; r < NVQ; ++r) {
-            const int u = tid + 256 * r;
-            if (u < C * M / EVT) *reinterpret_cast<uint4*>(sKr + u * EVT) = pk[r];
-        }
-#pragma unroll
-        for (int r = 0; r < NVV; ++r) {
-            const int u = tid + 256 * r;
-            if (u < C * DT / EVT) {
-                const int t = (u * EVT) / DT, c0 = (u * EVT) % DT;
-                const T* xe = reinterpret_cast<const T*>(&pv[r]);
-#pragma unroll
-                for (int e = 0; e < EVT; ++e) sVt[(c0 + e) * TP + t] = xe[e];
+            for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
+                const int n = rsub + RPT * j;
+                if (n < K) sA[rt * M + rI[rt * K + n]] = fmaxf(rA[rt * K + n], kAlphaMin);
             }
         }
-#pragma unroll
-        for (int r = 0; r < MAXRA; ++r) {
-            if (r < nra) {
-                const int u = tid + 256 * r;
-                const float av[4] = {pa[r].x, pa[r].y, pa[r].z, pa[r].w};
-                int t = div_small(4 * u, K, invK), n = 4 * u - t * K;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (t < nvalid && u < C * K / 4) sA[t * M + ((pi[r] >> (8 * e)) & 0xFF)] = fmaxf(av[e], kAlphaMin);
-                    if (++n == K) {
-                        n = 0;
-                        ++t;
-                    }
-                }
-            }
-        }
-        for (int i = Cfg::offK + tid * 16; i < 2 * Cfg::szQ; i += 256 * 16)
-            *reinterpret_cast<uint4*>(smem + i) = make_uint4(0u, 0u, 0u, 0u);
-        if (c + 1 < nC) {
-            load_qk(c + 1, pk, k);
-            load_v(c + 1);
-        }
-        __syncthreads();
+        for_each_tid<NPL * psQ / EVE, NT>(tid, [&](int i) {
+            *reinterpret_cast<uint4*>(sQK + (oK + i * EVE)) = make_uint4(0u, 0u, 0u, 0u);
+        });
+        wg_barrier();
 
         // ---- decay products: thread (slot i, part p) runs over its TPP tokens
         const int pslot = tid % M, ppart = tid / M;
-        float Eloc[TPP];
+        float Eloc[TPP], Aloc[DENSE ? TPP : 1];
         {
             float run = 1.0f;
 #pragma unroll
             for (int tt = 0; tt < TPP; ++tt) {
-                run *= sA[(ppart * TPP + tt) * M + pslot];
+                const int t = ppart * TPP + tt;
+                float a = sA[t * M + pslot];
+                if (DENSE) {
+                    a = t < nvalid ? a : 1.0f;
+                    Aloc[tt] = a;
+                    a = fmaxf(a, kAlphaMin);
+                }
+                run *= a;
                 Eloc[tt] = run;
             }
             sTot[ppart * M + pslot] = run;
         }
-        __syncthreads();
+        wg_barrier();
         int bad = 0;
         {
             float pre = 1.0f, last = 1.0f;
@@ -421,140 +431,151 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
                 last *= tp;
             }
 #pragma unroll
-            for (int tt = 0; tt < TPP; ++tt) sA[(ppart * TPP + tt) * M + pslot] = pre * Eloc[tt];
+            for (int tt = 0; tt < TPP; ++tt) {
+                const int t = ppart * TPP + tt;
+                const float ev = pre * Eloc[tt];
+                sA[t * M + pslot] = ev;
+                if (DENSE) {
+                    const float a = fmaxf(Aloc[tt], kAlphaMin);
+                    if (a < 1.0f)
+                        P::put(sQK, psQ, oK + t * QP + pslot,
+                               Elem<T>::load(rk, t * M + pslot) * (1.0f - a) * __builtin_amdgcn_rcpf(ev));
+                }
+            }
             if (ppart == 0) sE[pslot] = last;
             bad = !(last >= kSafeMin);
         }
-        const int unsafe = __syncthreads_or(bad);
+        {
+            const bool wave_bad = __ballot(bad) != 0;
+            if (lane == 0) sFlag[w] = wave_bad;
+        }
+        wg_barrier();
+        int unsafe = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) unsafe |= sFlag[i];
 
         if (unsafe) {
             // ---- exact token-by-token recurrence with the exact alphas
 #pragma unroll
             for (int j = 0; j < UPW; ++j) {
-                const int I = w + 4 * (j / NTD), D = j % NTD, i = 16 * I + l16;
+                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
                 if (I < NTM) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sHf[i * DT + 16 * D + 4 * q4 + r] = Hreg[j][r];
                 }
             }
+            if (DENSE) {
 #pragma unroll
-            for (int r = 0; r < MAXRA; ++r) {
-                const int u = tid + 256 * r;
-                if (r < nra && u < C * K / 4) {
-                    const float av[4] = {pa[r].x, pa[r].y, pa[r].z, pa[r].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sRa[4 * u + e] = av[e];
-                        sRi[4 * u + e] = uint8_t((pi[r] >> (8 * e)) & 0xFF);
-                    }
-                }
+                for (int tt = 0; tt < TPP; ++tt) sA[(ppart * TPP + tt) * M + pslot] = Aloc[tt];
             }
-            __syncthreads();
+            wg_barrier();
+            const int nent = DENSE ? M : K;
             for (int tt = 0; tt < nvalid; ++tt) {
-                const long row = (b * T_len + tokc + tt) * Hh + h;
-                for (int e = tid; e < K * DT; e += 256) {
+                for (int e = tid; e < nent * DT; e += NT) {
                     const int n = e / DT, dd = e % DT;
-                    const float a = sRa[tt * K + n];
-                    const int i = sRi[tt * K + n];
+                    const float a = DENSE ? sA[tt * M + n] : rA[tt * K + n];
+                    const int i = DENSE ? n : int(rI[tt * K + n]);
                     if (a != 1.0f) {
-                        const float wk = (1.0f - a) * Elem<T>::load(sKr, tt * M + i);
-                        const float vv = Elem<T>::load(sVt, dd * TP + tt);
-                        sHf[i * DT + dd] = fmaf(a, sHf[i * DT + dd], wk * vv);
+                        const float wk = (1.0f - a) * Elem<T>::load(rk, tt * M + i);
+                        sHf[i * DT + dd] = fmaf(a, sHf[i * DT + dd], wk * Elem<T>::load(rvc, tt * DT + dd));
                     }
                 }
-                __syncthreads();
+                wg_barrier();
                 if (tid < DT) {
                     float acc = 0.0f;
-                    for (int i = 0; i < M; ++i) acc = fmaf(Elem<T>::load(q + row * M, i), sHf[i * DT + tid], acc);
-                    o[row * Dv + d0 + tid] = acc;
+                    for (int i = 0; i < M; ++i) acc = fmaf(Elem<T>::load(rq, tt * M + i), sHf[i * DT + tid], acc);
+                    o[((b * T_len + tokc + tt) * rstride + h) * Dv + d0 + tid] = acc;
                 }
-                __syncthreads();
+                wg_barrier();
             }
 #pragma unroll
             for (int j = 0; j < UPW; ++j) {
-                const int I = w + 4 * (j / NTD), D = j % NTD, i = 16 * I + l16;
+                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
                 if (I < NTM) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Hreg[j][r] = sHf[i * DT + 16 * D + 4 * q4 + r];
-                    const int r0 = (16 * D + 4 * q4) * QP + i;
-                    P::put_pair(sHt, psHt, r0, r0 + QP, Hreg[j][0], Hreg[j][1]);
-                    P::put_pair(sHt, psHt, r0 + 2 * QP, r0 + 3 * QP, Hreg[j][2], Hreg[j][3]);
                 }
             }
-            __syncthreads();
-            for (int i = tid; i < C * M; i += 256) sA[i] = 1.0f;
-            if (c + 1 < nC) {
-                load_qk(c + 1, pq, q);
-                load_route(c + 1);
+            wg_barrier();  // every read of sHf (aliasing Qh/Kh) is done
+            if (MP > M)
+                for (int i = tid; i < NPL * psQ; i += NT) sQK[i] = E{};  // padding columns of Qh
+#pragma unroll
+            for (int j = 0; j < UPW; ++j) {
+                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
+                if (I < NTM)
+                    P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
             }
-            continue;
+            if (!DENSE)
+                for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
+            if (c + 1 < nC) {
+                issue_qk(c + 1);
+                issue_route(c + 1);
+            }
+            return;
         }
 
-        // ---- Qh = q o E (split planes) and Kh = k (1 - alpha) / E at the selected entries
+        // ---- Qh = q o E (split planes); compact route: Kh = k (1 - alpha) / E at its entries
+        constexpr int NQV = C * M / EVT;                    // 16-byte groups of q in the chunk
+        constexpr int QG = NQV > NT ? NQV / NT : 1;         // consecutive groups per thread
+        if (NQV >= NT || tid < NQV) {
+            const int t = (tid * QG * EVT) / M, i0 = (tid * QG * EVT) % M;
 #pragma unroll
-        for (int r = 0; r < NVQ; ++r) {
-            const int u = tid + 256 * r;
-            if (u < C * M / EVT) {
-                const int t = (u * EVT) / M, i0 = (u * EVT) % M;
+            for (int g = 0; g < QG; ++g) {
                 float qv[8];
-                unpack16(pq[r], qv, T());
-                const float* Ep = sA + t * M + i0;
+                unpack16(*reinterpret_cast<const uint4*>(rq + (t * M + i0 + g * EVT)), qv, T());
 #pragma unroll
-                for (int e = 0; e < EVT; ++e) qv[e] *= Ep[e];
-                P::put_vec(sQ, psQ, t * QP + i0, qv);
+                for (int e = 0; e < EVT; ++e) qv[e] *= sA[t * M + i0 + g * EVT + e];
+                P::put_vec(sQK, psQ, t * QP + i0 + g * EVT, qv);
             }
         }
+        if (!DENSE && rt < nvalid) {
 #pragma unroll
-        for (int r = 0; r < MAXRA; ++r) {
-            if (r < nra) {
-                const int u = tid + 256 * r;
-                const float av[4] = {pa[r].x, pa[r].y, pa[r].z, pa[r].w};
-                int t = div_small(4 * u, K, invK), n = 4 * u - t * K;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int slot = (pi[r] >> (8 * e)) & 0xFF;
-                    const float a = fmaxf(av[e], kAlphaMin);
-                    if (t < nvalid && u < C * K / 4 && a < 1.0f) {
-                        const float kh = Elem<T>::load(sKr, t * M + slot) * (1.0f - a) *
-                                         __builtin_amdgcn_rcpf(sA[t * M + slot]);
-                        P::put(sK, psQ, t * QP + slot, kh);
-                    }
-                    if (++n == K) {
-                        n = 0;
-                        ++t;
-                    }
+            for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
+                const int n = rsub + RPT * j;
+                if (n < K) {
+                    const int slot = rI[rt * K + n];
+                    const float a = fmaxf(rA[rt * K + n], kAlphaMin);
+                    if (a < 1.0f)
+                        P::put(sQK, psQ, oK + rt * QP + slot,
+                               Elem<T>::load(rk, rt * M + slot) * (1.0f - a) * __builtin_amdgcn_rcpf(sA[rt * M + slot]));
                 }
             }
         }
-        __syncthreads();
-        for (int i = tid; i < C * M; i += 256) sA[i] = 1.0f;  // ready for the next chunk's scatter
+        wg_barrier();
+        if (!DENSE)  // ready for the next chunk's scatter
+            for_each_tid<C * M / 4, NT>(tid, [&](int i) {
+                *reinterpret_cast<float4*>(sA + 4 * i) = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            });
         if (c + 1 < nC) {
-            load_qk(c + 1, pq, q);
-            load_route(c + 1);
+            issue_qk(c + 1);
+            issue_route(c + 1);
         }
 
         // ---- S^T = Kh Qh^T (masked) and O^T = V^T P^T + H_c^T Qh^T, one t-tile per wave
-        float* obase = o + ((b * T_len + tokc) * tstride + h) * Dv + d0;
-        for (int Tt = w; Tt < NTC; Tt += 4) {
+        float* obase = o + ((b * T_len + tokc) * rstride + h) * Dv + d0;
+#pragma unroll
+        for (int it = 0; it < (NTC + NW - 1) / NW; ++it) {
+            const int Tt = w + NW * it;
+            if (NTC % NW != 0 && Tt >= NTC) break;
             dfrag qf[NKM];
 #pragma unroll
             for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                 for (int pl = 0; pl < NPL; ++pl)
-                    qf[kb].p[pl] = P::ld(sQ + pl * psQ + (16 * Tt + l16) * QP + kb * KB + EPL * q4);
+                    qf[kb].p[pl] = P::ld(sQK, pl * psQ + (16 * Tt + l16) * QP + kb * KB + EPL * q4);
             floatx4 st[NTCP];
 #pragma unroll
             for (int J = 0; J < NTCP; ++J) {
                 st[J] = floatx4{0.f, 0.f, 0.f, 0.f};
                 if (J <= Tt && J < NTC) {
+                    dfrag a[NKM];
 #pragma unroll
-                    for (int kb = 0; kb < NKM; ++kb) {
-                        dfrag a;
+                    for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                         for (int pl = 0; pl < NPL; ++pl)
-                            a.p[pl] = P::ld(sK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
-                        st[J] = P::mm_dd(a, qf[kb], st[J]);
-                    }
+                            a[kb].p[pl] = P::ld(sQK, oK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
+#pragma unroll
+                    for (int kb = 0; kb < NKM; ++kb) st[J] = P::mm_dd(a[kb], qf[kb], st[J]);
                     if (J == Tt) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
@@ -568,24 +589,24 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             const int tl = 16 * Tt + l16;
 #pragma unroll
             for (int D = 0; D < NTD; ++D) {
-                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+                frag va[NKC];
+                dfrag ha[NKM];
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb) {
-                    if (kb * KB < 16 * (Tt + 1)) {
-                        const frag a = P::ld_perm(reinterpret_cast<const E*>(sVt) + (16 * D + l16) * TP, kb, q4);
-                        acc = P::mm_vd(a, pf[kb], acc);
-                    }
-                }
+                for (int kb = 0; kb < NKC; ++kb)
+                    va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);  // in bounds for every kb
 #pragma unroll
-                for (int kb = 0; kb < NKM; ++kb) {
-                    dfrag a;
+                for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl)
-                        a.p[pl] = P::ld(sHt + pl * psHt + (16 * D + l16) * QP + kb * KB + EPL * q4);
-                    acc = P::mm_dd(a, qf[kb], acc);
-                }
+                        ha[kb].p[pl] = P::template ld_col<false>(sH, pl * psH + 16 * D, HP, kb, q4, l16);
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb)
+                    if (kb * KB < 16 * (Tt + 1)) acc = P::mm_vd(va[kb], pf[kb], acc);
+#pragma unroll
+                for (int kb = 0; kb < NKM; ++kb) acc = P::mm_dd(ha[kb], qf[kb], acc);
                 if (tl < nvalid)
-                    *reinterpret_cast<float4*>(obase + tl * tstride * Dv + 16 * D + 4 * q4) =
+                    *reinterpret_cast<float4*>(obase + tl * rstride * Dv + 16 * D + 4 * q4) =
                         make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
         }
@@ -594,45 +615,49 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         floatx4 U[UPW];
 #pragma unroll
         for (int jI = 0; jI < NIW; ++jI) {
-            const int I = w + 4 * jI;
+            const int I = w + NW * jI;
 #pragma unroll
             for (int D = 0; D < NTD; ++D) U[jI * NTD + D] = floatx4{0.f, 0.f, 0.f, 0.f};
             if (I < NTM) {
+                dfrag kf[NKC];
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb) {
-                    dfrag bb;
+                for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
                     for (int pl = 0; pl < NPL; ++pl)
-                        bb.p[pl] = P::ld_perm_strided(sK + pl * psQ + 16 * I + l16, QP, kb, q4);
+                        kf[kb].p[pl] = P::template ld_col<true>(sQK, oK + pl * psQ + 16 * I, QP, kb, q4, l16);
 #pragma unroll
-                    for (int D = 0; D < NTD; ++D) {
-                        const frag a = P::ld_perm(reinterpret_cast<const E*>(sVt) + (16 * D + l16) * TP, kb, q4);
-                        U[jI * NTD + D] = P::mm_vd(a, bb, U[jI * NTD + D]);
-                    }
+                for (int D = 0; D < NTD; ++D) {
+                    frag va[NKC];
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb) va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb) U[jI * NTD + D] = P::mm_vd(va[kb], kf[kb], U[jI * NTD + D]);
                 }
             }
         }
-        __syncthreads();  // every read of H_c (sHt) is done
+        wg_barrier();  // every read of H_c (sH) is done
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int I = w + 4 * (j / NTD), D = j % NTD, i = 16 * I + l16;
+            const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
             if (I < NTM) {
                 const float e = sE[i];
                 if (e < 1.0f) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Hreg[j][r] = e * (Hreg[j][r] + U[j][r]);
-                    const int r0 = (16 * D + 4 * q4) * QP + i;
-                    P::put_pair(sHt, psHt, r0, r0 + QP, Hreg[j][0], Hreg[j][1]);
-                    P::put_pair(sHt, psHt, r0 + 2 * QP, r0 + 3 * QP, Hreg[j][2], Hreg[j][3]);
+                    P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
                 }
             }
         }
+    };
+    for (long c = 0; c < nC; c += 2) {
+        chunk(std::integral_constant<int, 0>{}, c);
+        if (c + 1 < nC) chunk(std::integral_constant<int, 1>{}, c + 1);
     }
 
     if (H_out) {
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int I = w + 4 * (j / NTD), D = j % NTD, i = 16 * I + l16;
+            const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
             if (I < NTM)
                 *reinterpret_cast<float4*>(H_out + (bh * M + i) * Dv + d0 + 16 * D + 4 * q4) =
                     make_float4(Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
@@ -651,16 +676,27 @@ __global__ void copy_state_kernel(const float* __restrict__ H0, float* __restric
 // ------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Chunk length the kernels run: the requested C, except fp32 inputs with M = 128, whose
+// C = 64 tiles do not fit in LDS and run as chunks of 32 (same result up to rounding).
+static int scan_chunk(int dtype, int M, int C) { return (dtype == RSM_F32 && M == 128 && C > 32) ? 32 : C; }
+
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K) {
-    (void)dtype;
     (void)Dv;
-    (void)M;
+    C = scan_chunk(dtype, M, C);
     FwdLayout L{};
+    L.chunk = C;
     L.n_chunks = (T + C - 1) / C;
+    L.dense = K > compact_cap(M) ? 1 : 0;
     const size_t rows = size_t(B) * size_t(Hh) * size_t(L.n_chunks) * size_t(C);  // padded token-heads
-    L.ridx_off = 0;
-    L.ralpha_off = align256(rows * size_t(K));
-    L.total = L.ralpha_off + align256(rows * size_t(K) * 4);
+    if (L.dense) {
+        L.ridx_off = 0;
+        L.ralpha_off = 0;
+        L.total = align256(rows * size_t(M) * 4);
+    } else {
+        L.ridx_off = 0;
+        L.ralpha_off = align256(rows * size_t(K));
+        L.total = L.ralpha_off + align256(rows * size_t(K) * 4);
+    }
     if (rows == 0) L.total = 0;
     return L;
 }
@@ -668,54 +704,55 @@ FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int 
 // Dv tile of the scan: 32 columns, 16 for M = 128 (LDS budget) or when Dv is 16.
 static int pick_dt(int M, int Dv) { return (M >= 128 || Dv % 32 != 0) ? 16 : 32; }
 
-template <typename T, int M, int C, int DT>
+template <typename T, int M, int C, int DT, bool DENSE>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
                        int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
                        hipStream_t s) {
-    typedef ScanCfg<T, M, C, DT> Cfg;
-    static bool attr_done = false;
-    if (!attr_done) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_scan_kernel<T, M, C, DT>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::total) != hipSuccess)
-            return RSM_ERR_HIP;
-        attr_done = true;
-    }
-    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT>), dim3(unsigned(B * Hh * (Dv / DT))), dim3(256), Cfg::total, s,
-                       q, k, v, H0, T_len, int(Hh), Dv, K, nC, ridx, ralpha, o, H_out);
+    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(B * Hh * (Dv / DT))), dim3(256), 0, s, q,
+                       k, v, H0, T_len, int(Hh), Dv, K, nC, ridx, ralpha, o, H_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
 template <typename T, int M, int C>
-static int dispatch_dt(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
-                       int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
+static int dispatch_dt(bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh,
+                       int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
                        hipStream_t s) {
-    if (pick_dt(M, Dv) == 32)
-        return launch_scan<T, M, C, 32>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-    return launch_scan<T, M, C, 16>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+    if (pick_dt(M, Dv) == 32) {
+        if constexpr (M < 128) {
+            if (dense) return launch_scan<T, M, C, 32, true>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+            return launch_scan<T, M, C, 32, false>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        }
+        return RSM_ERR_UNSUPPORTED;
+    }
+    if (dense) return launch_scan<T, M, C, 16, true>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+    return launch_scan<T, M, C, 16, false>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
 }
 
 template <typename T, int M>
-static int dispatch_c(int C, const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh,
-                      int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
-                      hipStream_t s) {
+static int dispatch_c(int C, bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len,
+                      long Hh, int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o,
+                      float* H_out, hipStream_t s) {
     switch (C) {
-        case 16: return dispatch_dt<T, M, 16>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 32: return dispatch_dt<T, M, 32>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 64: return dispatch_dt<T, M, 64>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 16: return dispatch_dt<T, M, 16>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 32: return dispatch_dt<T, M, 32>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 64:
+            if constexpr (sizeof(T) == 4 && M == 128) return RSM_ERR_UNSUPPORTED;
+            else return dispatch_dt<T, M, 64>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
     }
     return RSM_ERR_UNSUPPORTED;
 }
 
 template <typename T>
-static int dispatch_m(int M, int C, const void* q, const void* k, const void* v, const float* H0, long B,
+static int dispatch_m(int M, int C, bool dense, const void* q, const void* k, const void* v, const float* H0, long B,
                       long T_len, long Hh, int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o,
                       float* H_out, hipStream_t s) {
     const T *qq = static_cast<const T*>(q), *kk = static_cast<const T*>(k), *vv = static_cast<const T*>(v);
     switch (M) {
-        case 16: return dispatch_c<T, 16>(C, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 32: return dispatch_c<T, 32>(C, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 64: return dispatch_c<T, 64>(C, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 128: return dispatch_c<T, 128>(C, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 16: return dispatch_c<T, 16>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 32: return dispatch_c<T, 32>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 64: return dispatch_c<T, 64>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 128:
+            return dispatch_c<T, 128>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
     }
     return RSM_ERR_UNSUPPORTED;
 }
@@ -733,15 +770,18 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
         return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
     }
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
+    C = L.chunk;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     uint8_t* ridx = ws + L.ridx_off;
     float* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
     const long T_pad = L.n_chunks * C;
-    int st = route_fwd_launch(z, dtype, f, B, T, Hh, T_pad, M, K, idx_out, ridx, ralpha, stream);
+    int st = route_fwd_launch(z, dtype, f, B, T, Hh, T_pad, M, K, L.dense, idx_out, ridx, ralpha, stream);
     if (st != RSM_OK) return st;
     if (dtype == RSM_F32)
-        return dispatch_m<float>(M, C, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out, stream);
-    return dispatch_m<bf16_t>(M, C, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out, stream);
+        return dispatch_m<float>(M, C, L.dense, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out,
+                                 stream);
+    return dispatch_m<bf16_t>(M, C, L.dense, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out,
+                              stream);
 }
 
 }  // namespace rsm

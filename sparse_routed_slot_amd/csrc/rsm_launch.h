@@ -17,16 +17,19 @@ int decode_step_launch(const void* q, const void* k, const void* z, const void* 
                        const float* f, float* H, long n_heads, int M, int Dv, int K, float* o,
                        int32_t* idx_out, hipStream_t stream);
 
-// Workspace of the chunked forward: the compact route (slot uint8, alpha fp32) of every
-// token-head, in (batch*head, padded token) order; byte offsets and total.
+// Workspace of the chunked forward: the route of every token-head in (batch*head, padded
+// token) order, either compact (slot uint8 + alpha fp32 per selected slot) or dense (alpha
+// fp32 for every slot, used when K is a large fraction of M); byte offsets and total.
 struct FwdLayout {
     size_t ridx_off, ralpha_off, total;
     long n_chunks;
+    int dense;  // route as dense alphas [..][M] (K large) instead of (slot, alpha) lists
+    int chunk;  // chunk length the kernels run
 };
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream);
+                     int dense_out, int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream);
 
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,

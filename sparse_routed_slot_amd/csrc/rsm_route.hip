@@ -51,13 +51,16 @@ template <int M> struct RowRegs<float, M> {
 };
 
 // kFwd = false: public router (idx int32 [row][K], score [row][K] or NULL).
-// kFwd = true : forward router (ridx uint8 / ralpha fp32 at [(b*Hh + h)*T_pad + t][K],
-//               idx int32 [row][K] or NULL).
+// kFwd = true : forward router, rows written in (b*Hh + h, t) order with T_pad tokens per
+//               head: compact form (dense == 0) ridx uint8 / ralpha fp32 [..][K] in ascending
+//               slot order, or dense form (dense == 1) ralpha fp32 [..][M] with alpha for
+//               every slot (1 for unselected slots); idx int32 [row][K] or NULL either way.
 template <typename T, int M, bool kFwd>
 __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z, const float* __restrict__ f,
                                                         long n_rows, long T_len, int Hh, long T_pad, int K,
-                                                        int32_t* __restrict__ idx, float* __restrict__ score,
-                                                        uint8_t* __restrict__ ridx, float* __restrict__ ralpha) {
+                                                        int dense_out, int32_t* __restrict__ idx,
+                                                        float* __restrict__ score, uint8_t* __restrict__ ridx,
+                                                        float* __restrict__ ralpha) {
     typedef typename RowKey<T>::type U;
     extern __shared__ __align__(16) unsigned char smem[];
     int* s_slot = reinterpret_cast<int*>(smem);              // [K][64]
@@ -68,12 +71,40 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 
     RowRegs<T, M> x;
     x.load(z + row * M);
-    const bool dense = (K == M);
-    if (!dense) {
-        float v[M];
+    const bool all = (K == M);
+    float v[M];
 #pragma unroll
-        for (int i = 0; i < M; ++i) v[i] = x.val(i);
-        const U th = row_threshold<T, M>(v, K);
+    for (int i = 0; i < M; ++i) v[i] = x.val(i);
+    U th = 0;
+    if (!all) th = row_threshold<T, M>(v, K);
+    long dst = row * K;
+    float ft = 0.0f;
+    if (kFwd) {
+        const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
+        dst = ((b * Hh + h) * T_pad + t) * (dense_out ? M : K);
+        ft = f[row];
+    }
+    if (kFwd && dense_out) {
+        int n = 0;
+#pragma unroll
+        for (int i0 = 0; i0 < M; i0 += 4) {
+            float a4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + e;
+                a4[e] = 1.0f;
+                if (all || RowKey<T>::make(v[i], i) >= th) {
+                    const float s = sigmoidf_dev(v[i]);
+                    if (s > 0.0f) a4[e] = __expf(s * ft);
+                    if (idx) idx[row * K + n] = i;
+                    ++n;
+                }
+            }
+            *reinterpret_cast<float4*>(ralpha + dst + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+        }
+        return;
+    }
+    if (!all) {
         int n = 0;
 #pragma unroll
         for (int i = 0; i < M; ++i) {
@@ -84,16 +115,9 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
             }
         }
     }
-    long dst = row * K;
-    float ft = 0.0f;
-    if (kFwd) {
-        const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
-        dst = ((b * Hh + h) * T_pad + t) * K;
-        ft = f[row];
-    }
     for (int n = 0; n < K; ++n) {
-        const int i = dense ? n : s_slot[n * 64 + lane];
-        const float zi = dense ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane];
+        const int i = all ? n : s_slot[n * 64 + lane];
+        const float zi = all ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane];
         const float s = sigmoidf_dev(zi);
         if (kFwd) {
             ridx[dst + n] = uint8_t(i);
@@ -108,13 +132,14 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 
 template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K,
-                       int32_t* idx, float* score, uint8_t* ridx, float* ralpha, hipStream_t stream) {
+                       int dense_out, int32_t* idx, float* score, uint8_t* ridx, float* ralpha,
+                       hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
     const dim3 grid(unsigned((n_rows + 63) / 64)), block(64);
-    const size_t lds = size_t(K) * 64 * 8;
+    const size_t lds = (dense_out || K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane lists, compact form
 #define RSM_ROUTE_LAUNCH(MM)                                                                                    \
     hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, T_pad, \
-                       K, idx, score, ridx, ralpha)
+                       K, dense_out, idx, score, ridx, ralpha)
     switch (M) {
         case 16: RSM_ROUTE_LAUNCH(16); break;
         case 32: RSM_ROUTE_LAUNCH(32); break;
@@ -129,20 +154,20 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx, float* score,
                       hipStream_t stream) {
     if (dtype == RSM_F32)
-        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
-                                         nullptr, nullptr, stream);
-    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, 0, idx,
+                                         score, nullptr, nullptr, stream);
+    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, 0, idx, score,
                                       nullptr, nullptr, stream);
 }
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream) {
+                     int dense_out, int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream) {
     const long n_rows = B * T * Hh;
     if (dtype == RSM_F32)
-        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
-                                        nullptr, ridx, ralpha, stream);
-    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
-                                     nullptr, ridx, ralpha, stream);
+        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, dense_out,
+                                        idx_out, nullptr, ridx, ralpha, stream);
+    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, dense_out,
+                                     idx_out, nullptr, ridx, ralpha, stream);
 }
 
 }  // namespace rsm

@@ -33,10 +33,20 @@ def log(msg):
     sys.stdout.flush()
 
 
+def poison_pool(nbytes=1 << 28):
+    """Fill freed device memory with NaN so that any read of a buffer the library did not
+    write (workspace, outputs) shows up as a non-finite result."""
+    junk = torch.full((nbytes // 4,), float("nan"), device="cuda")
+    del junk
+
+
 def run_forward(rsm, d, K, C, want_idx=True):
+    poison_pool()
     t = dev_inputs(d, "cuda")
+    B, T, Hh, _ = d["q"].shape
+    out = torch.full((B, T, Hh, d["v"].shape[-1]), float("nan"), device="cuda")
     o, H, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=C, H0=t["H0"],
-                                    want_idx=want_idx)
+                                    want_idx=want_idx, out=out)
     torch.cuda.synchronize()
     return o.cpu().numpy(), H.cpu().numpy(), (idx.cpu().numpy() if want_idx else None)
 
