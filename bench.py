@@ -8,11 +8,12 @@ The decode step (256 sequences x 16 heads, M64 Dv128 K16, prefill T=512) is time
 same run: 1024 back-to-back rsm_decode_step calls between two HIP events.
 
 Prints one JSON line.  Inputs are synthetic (seeded generator), already resident in HBM
-when the timed region starts.  `--gpus N` with N > 1 is refused: this build is one GPU.
+when the timed region starts.  The benchmark runs on one GPU: `--gpus N` with N > 1 is refused.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +26,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "RSM forward tokens/s (B8 T2048 M64) + decode-step µs; % HBM/MFMA roofline"
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+# Sources of the two forward kernels; the stored counter figures hold only for these bytes.
+FWD_SOURCES = ["rsm_forward.hip", "rsm_route.hip", "rsm_device.h", "rsm_launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_fwd_b8_t2048_traffic.txt")
 
 
 def forward_bytes(B, T, Hh, M, Dv, es):
@@ -39,6 +44,26 @@ def decode_bytes(B, Hh, M, Dv, K, es):
             + B * Hh * 4 + B * Hh * Dv * 4)
 
 
+def forward_sources_sha256():
+    h = hashlib.sha256()
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "sparse_routed_slot_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per forward call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (copy-calibrated), or None when the kernel sources changed since they were taken."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != forward_sources_sha256():
+        return None
+    return float(fields["hbm_bytes_per_call"])
+
+
 def to_dev(d, torch):
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -46,19 +71,25 @@ def to_dev(d, torch):
             "f": torch.from_numpy(d["f"]).cuda()}
 
 
-def cpu_baseline(w, d):
-    """The float64 oracle, as is, on the host cores: the full forward workload."""
+def cpu_baseline(w, d, min_seconds=10.0):
+    """The float64 oracle, as is, on the host cores: the whole forward workload, repeated
+    until about ten seconds of wall time have passed."""
     from oracle import oracle
     from sparse_routed_slot_amd import inputs as gen
     r = {n: gen.as_f64(d[n], "bf16") for n in "qkzv"}
     f = d["f"].astype(np.float64)
     threads = oracle.max_threads()
+    reps = 0
     t0 = time.perf_counter()
-    oracle.forward(r["q"], r["k"], r["z"], r["v"], f, w.K)
-    dt = time.perf_counter() - t0
-    return {"value": w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"full forward workload (B{w.B} T{w.T} Hh{w.Hh} M{w.M} Dv{w.Dv} K{w.K}), "
-                      f"float64 recurrence, {dt:.2f} s wall on {threads} threads"}
+    while True:
+        oracle.forward(r["q"], r["k"], r["z"], r["v"], f, w.K)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": reps * w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x the full forward workload (B{w.B} T{w.T} Hh{w.Hh} M{w.M} Dv{w.Dv} "
+                      f"K{w.K}), float64 recurrence, {dt:.1f} s wall on {threads} threads"}
 
 
 def main():
@@ -68,9 +99,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads, batch and value columns shard with no communication; see the sharding notes)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -121,6 +155,14 @@ def main():
     print(f"[bench] forward: wall {ms_per_step * 1e3:.1f} us/step, events {kernel_ms * 1e3:.1f} us "
           f"(min {min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---------------------------------------------------------------- decode
     wd = gen.WORKLOADS["decode_b256"]
     print(f"[bench] decode: prefill T={wd.T} for {wd.B}x{wd.Hh} heads", file=sys.stderr, flush=True)
@@ -170,8 +212,9 @@ def main():
         "decode_config": {"workload": wd.name, "B": wd.B, "Hh": wd.Hh, "M": wd.M, "Dv": wd.Dv, "K": wd.K,
                           "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": len(pool)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "rsm_forward_chunked = fwd_prep_kernel + fwd_scan_kernel",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
+                     "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel "
+                               "(two launches back to back on the caller's stream)",
                      "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
