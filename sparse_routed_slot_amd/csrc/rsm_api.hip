@@ -77,7 +77,7 @@ size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, 
                                    int64_t C, int64_t K) {
     if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv) || !c_ok(C)) return 0;
     if (K < 1 || K > M) return 0;
-    if (mul_ck({B, T + C, Hh, M, 5}) < 0) return 0;
+    if (mul_ck({B, T + C, Hh, M, 5}) < 0 || mul_ck({B, Hh, T / C + 2, M, Dv, 4}) < 0) return 0;
     return rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C), int(K)).total;
 }
 

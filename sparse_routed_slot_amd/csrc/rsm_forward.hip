@@ -240,19 +240,43 @@ __device__ __forceinline__ void wg_barrier() {
 constexpr int compact_cap(int M) { return M / 2 < 32 ? M / 2 : 32; }
 
 // ------------------------------------------------------------------------------------
-// Scan: one workgroup (4 waves) per (b, h, Dv tile of DT columns); sequential over chunks.
+// Sequence segments.  A head's chunks are cut into S consecutive segments so that a launch
+// has enough workgroups.  Segment s starts from the state the segments before it leave:
+//     H_start(s+1) = diag(E_s) H_start(s) + dH_s,
+// with E_s the product of the decay factors over segment s and dH_s the state segment s
+// reaches from a zero state (the recurrence is linear in the state).  Pass A computes
+// (E_s, dH_s) for every segment but the last and emits nothing else; pass B folds them into
+// its start state and runs its segment with outputs.  With S = 1 there is only pass B.
+// ------------------------------------------------------------------------------------
+struct SegArgs {
+    long nC;    // chunks in the sequence
+    int S;      // segments
+    int cps;    // chunks per segment
+    float* dH;  // [B*Hh][S-1][M][Dv]
+    float* dE;  // [B*Hh][S-1][M]
+};
+
+// ------------------------------------------------------------------------------------
+// Chunk scan: one workgroup (8 waves) per (b, h, Dv tile of DT columns, segment); it walks
+// the segment's chunks in order with the fp32 state tile in registers.
 // DENSE: the route arrives as dense alphas [C][M] instead of (slot, alpha) lists.
+// pass_a: pass A of the segment split (no Qh, no outputs; writes dH, dE).
+//
+// Wave roles (w = 0..7, all uniform):
+//  * chunk-row tile Tt of S^T and O^T: waves w and w + NTC*g share Tt; odd groups take the
+//    tiles in reverse so that the two waves of a SIMD (w, w+4) get a cheap and a costly tile;
+//  * slot tile I = w % NTM of U^T and of the state, column tiles gI, gI + GI, ...
 // ------------------------------------------------------------------------------------
 template <typename T, int M, int C, int DT, bool DENSE>
-__global__ __launch_bounds__(256) void fwd_scan_kernel(
+__global__ __launch_bounds__(512) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
-    long T_len, int Hh, int Dv, int K, long nC, const uint8_t* __restrict__ ridx, const float* __restrict__ ralpha,
-    float* __restrict__ o, float* __restrict__ H_out) {
+    long T_len, int Hh, int Dv, int K, SegArgs sg, int pass_a, const uint8_t* __restrict__ ridx,
+    const float* __restrict__ ralpha, float* __restrict__ o, float* __restrict__ H_out) {
     typedef Pol<T> P;
     typedef typename P::E E;
     typedef typename P::frag frag;
     typedef typename P::dfrag dfrag;
-    constexpr int NW = 4, NT = 64 * NW;
+    constexpr int NW = 8, NT = 64 * NW;
     constexpr int KB = P::KB, EPL = P::EPL, NPL = P::NPL;
     constexpr int MP = M > KB ? M : KB;        // padded slot dimension (k of slot contractions)
     constexpr int CP = C > KB ? C : KB;        // padded chunk dimension (k of row contractions)
@@ -260,12 +284,21 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     constexpr int QP = MP + EVE;               // pitch of Qh / Kh rows
     constexpr int HP = DT + EVE;               // pitch of state rows
     constexpr int NTC = C / 16, NTCP = CP / 16, NTD = DT / 16, NTM = M / 16;
-    constexpr int NIW = (NTM + NW - 1) / NW;  // slot tiles per wave (I = w + NW*jI)
-    constexpr int UPW = NIW * NTD;             // state tiles per wave
     constexpr int NKM = MP / KB, NKC = CP / KB;
-    constexpr int NPART = NT / M, TPP = C / NPART;
+    constexpr int GT = NW / NTC;               // waves per chunk-row tile
+    constexpr int NOD = (NTD + GT - 1) / GT;   // output column tiles per wave
+    constexpr int GI = NW / NTM;               // waves per slot tile
+    constexpr int UPW = (NTD + GI - 1) / GI;   // state tiles per wave
+    constexpr int NPART = NT / M < C ? NT / M : C;  // token parts of the decay products
+    constexpr int TPP = C / NPART;
     constexpr int KC = compact_cap(M);
-    constexpr int EVT = 16 / int(sizeof(T));
+    constexpr int RPT = NT / C;                // threads per token for the compact route
+    constexpr int psQ = CP * QP + 8;           // plane stride of Qh / Kh
+    constexpr int oK = NPL * psQ;              // Kh planes start here
+    constexpr int psH = MP * HP;               // plane stride of the state copy
+    constexpr int SZQK = 2 * NPL * psQ;
+    constexpr int SZHF = M * DT * 4 / int(sizeof(E));
+    static_assert(NW % NTC == 0 && NW % NTM == 0 && NT % C == 0, "tile split");
 
     // LDS.  Raw inputs land by direct loads (tile arrays padded to 1 KB); every array is a
     // separate object so the compiler can tell the direct loads from the other accesses.
@@ -275,110 +308,132 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
     __shared__ __align__(16) T rv1[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, odd chunks
     __shared__ __align__(16) float rA[DENSE ? 4 : pad1k(C * KC * 4) / 4];
     __shared__ __align__(16) uint8_t rI[DENSE ? 16 : pad1k(C * KC)];
-    __shared__ __align__(16) float sA[pad1k(C * M * 4) / 4];  // alphas -> decay products E
-    __shared__ __align__(16) E sQK[2 * NPL * (CP * QP + 8)];  // Qh planes, then Kh planes
-    __shared__ __align__(16) E sH[NPL * MP * HP];             // state copy, row-major [i][d]
+    __shared__ __align__(16) float sA[pad1k(C * M * 4) / 4];        // exact alphas of the chunk
+    __shared__ __align__(16) E sQK[SZQK > SZHF ? SZQK : SZHF];      // Qh planes, then Kh planes
+    __shared__ __align__(16) E sH[NPL * psH];                       // state copy, row-major [i][d]
     __shared__ float sTot[NPART * M];
     __shared__ float sE[M];
     __shared__ int sFlag[NW];
-    constexpr int psQ = CP * QP + 8;                          // plane stride of Qh / Kh
-    constexpr int psH = MP * HP;                              // plane stride of the state copy
-    constexpr int oK = NPL * psQ;                             // Kh planes start here
-    float* sHf = reinterpret_cast<float*>(sQK);               // exact path: state [M][DT]
-    static_assert(M * DT * 4 <= int(sizeof(sQK)), "exact-path state must fit in the Qh/Kh area");
+    float* sHf = reinterpret_cast<float*>(sQK);  // exact path: fp32 state [M][DT]
 
-    // workgroup -> (head, Dv tile); the Dv tiles of one head land on the same XCD
-    // (workgroups are dealt to the 8 XCDs round-robin) so they share inputs in its L2.
+    // workgroup -> (head, segment, Dv tile); consecutive ids (the Dv tiles of one head and
+    // segment) land on the same XCD (workgroups are dealt to the 8 XCDs round-robin)
     const int nDT = Dv / DT;
+    const int nseg = pass_a ? sg.S - 1 : sg.S;
     const long nblk = gridDim.x;
     long id = blockIdx.x;
     if (nblk % 8 == 0) id = (long(blockIdx.x) % 8) * (nblk / 8) + long(blockIdx.x) / 8;
-    const long bh = id / nDT;
-    const int d0 = int(id % nDT) * DT;
+    const int dtile = int(id % nDT);
+    const long rest = id / nDT;
+    const int seg = int(rest % nseg);
+    const long bh = rest / nseg;
+    const int d0 = dtile * DT;
     const long h = bh % Hh, b = bh / Hh;
-    const long T_pad = nC * C;
+    const long T_pad = sg.nC * C;
+    const long c_begin = long(seg) * sg.cps;
+    const long c_end = c_begin + sg.cps < sg.nC ? c_begin + sg.cps : sg.nC;
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     // wave index in a scalar register: every branch on it is a uniform scalar branch (no
     // EXEC masking around the MFMAs, which would not be skipped lane by lane)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // compact route entries: thread -> token rt, entries rsub, rsub + RPT, ... (< K)
-    constexpr int RPT = NT / C;
-    const int rt = tid / RPT, rsub = tid % RPT;
-    const long rstride = long(Hh);  // rows between consecutive tokens of one head
+    const int gT = w / NTC;
+    const int Tt = (gT & 1) ? NTC - 1 - w % NTC : w % NTC;
+    const int I = w % NTM, gI = w / NTM;
+    const int rt = tid / RPT, rsub = tid % RPT;     // compact route entries: token, first entry
+    const int pslot = tid % M, ppart = tid / M;     // decay products: slot, token part
+    const long rstride = long(Hh);                  // rows between consecutive tokens of one head
+    const long segrow = (bh * (sg.S - 1) + seg) * M;  // row of this segment in dH / dE
 
     // ---- direct loads of chunk c's inputs (rows past the sequence end repeat the last row;
     // their tokens carry no route entries, so they contribute nothing)
     auto issue_qk = [&](long c) {
         const int nv = int(T_len - c * C < C ? T_len - c * C : C);
-        const char* qb = reinterpret_cast<const char*>(q + ((b * T_len + c * C) * rstride + h) * M);
-        const char* kb_ = reinterpret_cast<const char*>(k + ((b * T_len + c * C) * rstride + h) * M);
         constexpr int RB = M * int(sizeof(T));
-        auto fq = [&](int off) {
-            const int t = min(off / RB, nv - 1), cb = off % RB;
-            return static_cast<const void*>(qb + long(t) * rstride * RB + cb);
-        };
-        auto fk = [&](int off) {
+        const char* kb_ = reinterpret_cast<const char*>(k + ((b * T_len + c * C) * rstride + h) * M);
+        dma_tile<NW>(rk, int(sizeof(rk)), w, lane, [&](int off) {
             const int t = min(off / RB, nv - 1), cb = off % RB;
             return static_cast<const void*>(kb_ + long(t) * rstride * RB + cb);
-        };
-        dma_tile<NW>(rq, int(sizeof(rq)), w, lane, fq);
-        dma_tile<NW>(rk, int(sizeof(rk)), w, lane, fk);
+        });
+        if (!pass_a) {
+            const char* qb = reinterpret_cast<const char*>(q + ((b * T_len + c * C) * rstride + h) * M);
+            dma_tile<NW>(rq, int(sizeof(rq)), w, lane, [&](int off) {
+                const int t = min(off / RB, nv - 1), cb = off % RB;
+                return static_cast<const void*>(qb + long(t) * rstride * RB + cb);
+            });
+        }
     };
     auto issue_v = [&](long c, T* dst) {
         const int nv = int(T_len - c * C < C ? T_len - c * C : C);
         const char* vb = reinterpret_cast<const char*>(v + ((b * T_len + c * C) * rstride + h) * Dv + d0);
         constexpr int RB = DT * int(sizeof(T));
         const long gpitch = rstride * Dv * long(sizeof(T));
-        auto fv = [&](int off) {
+        dma_tile<NW>(dst, int(sizeof(rv0)), w, lane, [&](int off) {
             const int t = min(off / RB, nv - 1), cb = off % RB;
             return static_cast<const void*>(vb + t * gpitch + cb);
-        };
-        dma_tile<NW>(dst, int(sizeof(rv0)), w, lane, fv);
+        });
     };
     auto issue_route = [&](long c) {
         if (DENSE) {
             const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * M);
-            auto fa = [&](int off) { return static_cast<const void*>(ab + min(off, C * M * 4 - 16)); };
-            dma_tile<NW>(sA, int(sizeof(sA)), w, lane, fa);
+            dma_tile<NW>(sA, int(sizeof(sA)), w, lane,
+                         [&](int off) { return static_cast<const void*>(ab + min(off, C * M * 4 - 16)); });
         } else {
             const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * K);
             const char* ib = reinterpret_cast<const char*>(ridx + (bh * T_pad + c * C) * K);
             const int na = C * K * 4, ni = C * K;
-            auto fa = [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); };
-            auto fi = [&](int off) { return static_cast<const void*>(ib + min(off, ni - 16)); };
-            dma_tile<NW>(rA, pad1k(na), w, lane, fa);
-            dma_tile<NW>(rI, pad1k(ni), w, lane, fi);
+            dma_tile<NW>(rA, pad1k(na), w, lane,
+                         [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); });
+            dma_tile<NW>(rI, pad1k(ni), w, lane,
+                         [&](int off) { return static_cast<const void*>(ib + min(off, ni - 16)); });
         }
     };
 
-    // ---- initial state: registers (tile j = jI*NTD + D holds H[16*I + l16][16*D + 4*q4 + r]).
-    // Padding (slot rows past M, chunk rows past C when a k-block is longer) stays zero.
+    // ---- start state in registers: tile j holds H[16*I + l16][16*D + 4*q4 + r], D = gI + GI*j.
+    // Pass B starts from H0 (or zero) and folds in the segments before its own; pass A
+    // starts from zero.  LDS padding (slot rows past M, chunk rows past C) stays zero.
     for (int i = tid; i < int(sizeof(sQK) / sizeof(E)); i += NT) sQK[i] = E{};
     for (int i = tid; i < int(sizeof(sH) / sizeof(E)); i += NT) sH[i] = E{};
-    wg_barrier();
     floatx4 Hreg[UPW];
+    float Eseg = 1.0f;  // pass A: decay product over the segment of row 16*I + l16
 #pragma unroll
     for (int j = 0; j < UPW; ++j) {
-        const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
+        const int D = gI + GI * j, i = 16 * I + l16, col = d0 + 16 * D + 4 * q4;
         Hreg[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (I < NTM) {
+        if (!pass_a && D < NTD) {
             if (H0) {
-                const float4 x = *reinterpret_cast<const float4*>(H0 + (bh * M + i) * Dv + d0 + 16 * D + 4 * q4);
+                const float4 x = *reinterpret_cast<const float4*>(H0 + (bh * M + i) * Dv + col);
                 Hreg[j] = floatx4{x.x, x.y, x.z, x.w};
             }
-            P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+            for (int sj = 0; sj < seg; ++sj) {
+                const long row = (bh * (sg.S - 1) + sj) * M + i;
+                const float e = sg.dE[row];
+                if (e != 1.0f) {  // rows untouched in segment sj keep their bits
+                    const float4 x = *reinterpret_cast<const float4*>(sg.dH + row * Dv + col);
+                    Hreg[j] = floatx4{fmaf(e, Hreg[j][0], x.x), fmaf(e, Hreg[j][1], x.y),
+                                      fmaf(e, Hreg[j][2], x.z), fmaf(e, Hreg[j][3], x.w)};
+                }
+            }
         }
     }
-    if (nC > 0) {
-        issue_qk(0);
-        issue_v(0, rv0);
-        issue_route(0);
+    wg_barrier();  // the zero fill is done before the state copy is written
+    if (!pass_a) {
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+            const int D = gI + GI * j, i = 16 * I + l16;
+            if (D < NTD) P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+        }
+    }
+    if (c_begin < c_end) {
+        issue_qk(c_begin);
+        issue_v(c_begin, rv0);
+        issue_route(c_begin);
     }
     if (!DENSE)
         for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
 
-    // One chunk.  CUR selects the v buffer statically (even chunks rv0, odd chunks rv1) so
-    // the compiler can tell the in-flight loads of the next chunk's v from this chunk's reads.
+    // One chunk.  CUR selects the v buffer statically (even chunks of the segment rv0, odd
+    // rv1) so the compiler can tell the in-flight loads of the next chunk's v from this
+    // chunk's reads.
     auto chunk = [&](auto cur, long c) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur)::value;
         const long tokc = c * C;
@@ -386,61 +441,56 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         const T* rvc = CUR ? rv1 : rv0;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
         wg_barrier();                   // ... and every other wave's
-        if (c + 1 < nC) issue_v(c + 1, CUR ? rv0 : rv1);
+        if (c + 1 < c_end) issue_v(c + 1, CUR ? rv0 : rv1);
 
-        // ---- scatter the clamped alphas (compact route), clear Kh
-        if (!DENSE && rt < nvalid) {
+        // ---- compact route: scatter the exact alphas into the dense tile (1 elsewhere)
+        if (!DENSE) {
+            if (rt < nvalid) {
 #pragma unroll
-            for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
-                const int n = rsub + RPT * j;
-                if (n < K) sA[rt * M + rI[rt * K + n]] = fmaxf(rA[rt * K + n], kAlphaMin);
+                for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
+                    const int n = rsub + RPT * j;
+                    if (n < K) sA[rt * M + rI[rt * K + n]] = rA[rt * K + n];
+                }
             }
+            wg_barrier();
         }
-        for_each_tid<NPL * psQ / EVE, NT>(tid, [&](int i) {
-            *reinterpret_cast<uint4*>(sQK + (oK + i * EVE)) = make_uint4(0u, 0u, 0u, 0u);
-        });
-        wg_barrier();
 
-        // ---- decay products: thread (slot i, part p) runs over its TPP tokens
-        const int pslot = tid % M, ppart = tid / M;
-        float Eloc[TPP], Aloc[DENSE ? TPP : 1];
-        {
+        // ---- decay products: thread (slot pslot, part ppart) runs over its TPP tokens with
+        // the clamped alphas; the parts' products are combined through LDS
+        float Eloc[TPP], Aloc[TPP];
+        if (ppart < NPART) {
             float run = 1.0f;
 #pragma unroll
             for (int tt = 0; tt < TPP; ++tt) {
                 const int t = ppart * TPP + tt;
-                float a = sA[t * M + pslot];
-                if (DENSE) {
-                    a = t < nvalid ? a : 1.0f;
-                    Aloc[tt] = a;
-                    a = fmaxf(a, kAlphaMin);
-                }
-                run *= a;
+                const float a = t < nvalid ? sA[t * M + pslot] : 1.0f;
+                Aloc[tt] = a;
+                run *= fmaxf(a, kAlphaMin);
                 Eloc[tt] = run;
             }
             sTot[ppart * M + pslot] = run;
         }
         wg_barrier();
+
+        // ---- E, and in the same pass Qh = q o E and Kh = k (1 - alpha) / E (0 where alpha = 1)
         int bad = 0;
-        {
+        if (ppart < NPART) {
             float pre = 1.0f, last = 1.0f;
 #pragma unroll
             for (int p = 0; p < NPART; ++p) {
                 const float tp = sTot[p * M + pslot];
-                if (p < ppart) pre *= tp;
+                pre = p < ppart ? pre * tp : pre;
                 last *= tp;
             }
 #pragma unroll
             for (int tt = 0; tt < TPP; ++tt) {
                 const int t = ppart * TPP + tt;
                 const float ev = pre * Eloc[tt];
-                sA[t * M + pslot] = ev;
-                if (DENSE) {
-                    const float a = fmaxf(Aloc[tt], kAlphaMin);
-                    if (a < 1.0f)
-                        P::put(sQK, psQ, oK + t * QP + pslot,
-                               Elem<T>::load(rk, t * M + pslot) * (1.0f - a) * __builtin_amdgcn_rcpf(ev));
-                }
+                if (!pass_a) P::put(sQK, psQ, t * QP + pslot, Elem<T>::load(rq, t * M + pslot) * ev);
+                const float a = fmaxf(Aloc[tt], kAlphaMin);
+                const float kh =
+                    a < 1.0f ? Elem<T>::load(rk, t * M + pslot) * (1.0f - a) * __builtin_amdgcn_rcpf(ev) : 0.0f;
+                P::put(sQK, psQ, oK + t * QP + pslot, kh);
             }
             if (ppart == 0) sE[pslot] = last;
             bad = !(last >= kSafeMin);
@@ -455,108 +505,80 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
         for (int i = 0; i < NW; ++i) unsafe |= sFlag[i];
 
         if (unsafe) {
-            // ---- exact token-by-token recurrence with the exact alphas
+            // ---- exact token-by-token recurrence with the exact alphas, on an fp32 copy
 #pragma unroll
             for (int j = 0; j < UPW; ++j) {
-                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
-                if (I < NTM) {
+                const int D = gI + GI * j, i = 16 * I + l16;
+                if (D < NTD) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sHf[i * DT + 16 * D + 4 * q4 + r] = Hreg[j][r];
                 }
             }
-            if (DENSE) {
-#pragma unroll
-                for (int tt = 0; tt < TPP; ++tt) sA[(ppart * TPP + tt) * M + pslot] = Aloc[tt];
-            }
             wg_barrier();
-            const int nent = DENSE ? M : K;
             for (int tt = 0; tt < nvalid; ++tt) {
-                for (int e = tid; e < nent * DT; e += NT) {
-                    const int n = e / DT, dd = e % DT;
-                    const float a = DENSE ? sA[tt * M + n] : rA[tt * K + n];
-                    const int i = DENSE ? n : int(rI[tt * K + n]);
+                for (int e = tid; e < M * DT; e += NT) {
+                    const int i = e / DT, dd = e % DT;
+                    const float a = sA[tt * M + i];
                     if (a != 1.0f) {
                         const float wk = (1.0f - a) * Elem<T>::load(rk, tt * M + i);
-                        sHf[i * DT + dd] = fmaf(a, sHf[i * DT + dd], wk * Elem<T>::load(rvc, tt * DT + dd));
+                        sHf[e] = fmaf(a, sHf[e], wk * Elem<T>::load(rvc, tt * DT + dd));
                     }
                 }
                 wg_barrier();
-                if (tid < DT) {
+                if (!pass_a && tid < DT) {
                     float acc = 0.0f;
                     for (int i = 0; i < M; ++i) acc = fmaf(Elem<T>::load(rq, tt * M + i), sHf[i * DT + tid], acc);
                     o[((b * T_len + tokc + tt) * rstride + h) * Dv + d0 + tid] = acc;
                 }
                 wg_barrier();
             }
+            if (tid < M) {  // decay product of the chunk with the exact alphas
+                float e = 1.0f;
+                for (int tt = 0; tt < nvalid; ++tt) e *= sA[tt * M + tid];
+                sE[tid] = e;
+            }
 #pragma unroll
             for (int j = 0; j < UPW; ++j) {
-                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
-                if (I < NTM) {
+                const int D = gI + GI * j, i = 16 * I + l16;
+                if (D < NTD) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Hreg[j][r] = sHf[i * DT + 16 * D + 4 * q4 + r];
                 }
             }
-            wg_barrier();  // every read of sHf (aliasing Qh/Kh) is done
-            if (MP > M)
-                for (int i = tid; i < NPL * psQ; i += NT) sQK[i] = E{};  // padding columns of Qh
+            wg_barrier();  // every read of sHf (aliasing Qh/Kh) is done; sE is written
+            if (MP > M || CP > C)
+                for (int i = tid; i < int(sizeof(sQK) / sizeof(E)); i += NT) sQK[i] = E{};  // padding
+            if (!pass_a) {
 #pragma unroll
-            for (int j = 0; j < UPW; ++j) {
-                const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
-                if (I < NTM)
-                    P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+                for (int j = 0; j < UPW; ++j) {
+                    const int D = gI + GI * j, i = 16 * I + l16;
+                    if (D < NTD)
+                        P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+                }
+            } else {
+                Eseg *= sE[16 * I + l16];
             }
             if (!DENSE)
                 for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
-            if (c + 1 < nC) {
+            if (c + 1 < c_end) {
                 issue_qk(c + 1);
                 issue_route(c + 1);
             }
             return;
         }
 
-        // ---- Qh = q o E (split planes); compact route: Kh = k (1 - alpha) / E at its entries
-        constexpr int NQV = C * M / EVT;                    // 16-byte groups of q in the chunk
-        constexpr int QG = NQV > NT ? NQV / NT : 1;         // consecutive groups per thread
-        if (NQV >= NT || tid < NQV) {
-            const int t = (tid * QG * EVT) / M, i0 = (tid * QG * EVT) % M;
-#pragma unroll
-            for (int g = 0; g < QG; ++g) {
-                float qv[8];
-                unpack16(*reinterpret_cast<const uint4*>(rq + (t * M + i0 + g * EVT)), qv, T());
-#pragma unroll
-                for (int e = 0; e < EVT; ++e) qv[e] *= sA[t * M + i0 + g * EVT + e];
-                P::put_vec(sQK, psQ, t * QP + i0 + g * EVT, qv);
-            }
-        }
-        if (!DENSE && rt < nvalid) {
-#pragma unroll
-            for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
-                const int n = rsub + RPT * j;
-                if (n < K) {
-                    const int slot = rI[rt * K + n];
-                    const float a = fmaxf(rA[rt * K + n], kAlphaMin);
-                    if (a < 1.0f)
-                        P::put(sQK, psQ, oK + rt * QP + slot,
-                               Elem<T>::load(rk, rt * M + slot) * (1.0f - a) * __builtin_amdgcn_rcpf(sA[rt * M + slot]));
-                }
-            }
-        }
-        wg_barrier();
         if (!DENSE)  // ready for the next chunk's scatter
             for_each_tid<C * M / 4, NT>(tid, [&](int i) {
                 *reinterpret_cast<float4*>(sA + 4 * i) = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
             });
-        if (c + 1 < nC) {
+        if (c + 1 < c_end) {
             issue_qk(c + 1);
             issue_route(c + 1);
         }
 
-        // ---- S^T = Kh Qh^T (masked) and O^T = V^T P^T + H_c^T Qh^T, one t-tile per wave
-        float* obase = o + ((b * T_len + tokc) * rstride + h) * Dv + d0;
-#pragma unroll
-        for (int it = 0; it < (NTC + NW - 1) / NW; ++it) {
-            const int Tt = w + NW * it;
-            if (NTC % NW != 0 && Tt >= NTC) break;
+        // ---- S^T = Kh Qh^T (masked) and O^T = V^T P^T + H_c^T Qh^T for chunk-row tile Tt
+        if (!pass_a) {
+            float* obase = o + ((b * T_len + tokc) * rstride + h) * Dv + d0;
             dfrag qf[NKM];
 #pragma unroll
             for (int kb = 0; kb < NKM; ++kb)
@@ -588,7 +610,9 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             for (int kb = 0; kb < NKC; ++kb) pf[kb] = P::pack_perm(st, kb);
             const int tl = 16 * Tt + l16;
 #pragma unroll
-            for (int D = 0; D < NTD; ++D) {
+            for (int jd = 0; jd < NOD; ++jd) {
+                const int D = gT + GT * jd;
+                if (NTD % GT != 0 && D >= NTD) break;
                 frag va[NKC];
                 dfrag ha[NKM];
 #pragma unroll
@@ -611,54 +635,61 @@ __global__ __launch_bounds__(256) void fwd_scan_kernel(
             }
         }
 
-        // ---- U^T = V^T Kh on the state tiles this wave owns (Kh fragments shared across D)
+        // ---- U^T = V^T Kh on the state tiles of this wave (Kh fragments shared across D)
         floatx4 U[UPW];
+        {
+            dfrag kf[NKC];
 #pragma unroll
-        for (int jI = 0; jI < NIW; ++jI) {
-            const int I = w + NW * jI;
+            for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
-            for (int D = 0; D < NTD; ++D) U[jI * NTD + D] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (I < NTM) {
-                dfrag kf[NKC];
+                for (int pl = 0; pl < NPL; ++pl)
+                    kf[kb].p[pl] = P::template ld_col<true>(sQK, oK + pl * psQ + 16 * I, QP, kb, q4, l16);
 #pragma unroll
-                for (int kb = 0; kb < NKC; ++kb)
-#pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl)
-                        kf[kb].p[pl] = P::template ld_col<true>(sQK, oK + pl * psQ + 16 * I, QP, kb, q4, l16);
-#pragma unroll
-                for (int D = 0; D < NTD; ++D) {
+            for (int j = 0; j < UPW; ++j) {
+                const int D = gI + GI * j;
+                U[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (D < NTD) {
                     frag va[NKC];
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb) va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);
 #pragma unroll
-                    for (int kb = 0; kb < NKC; ++kb) U[jI * NTD + D] = P::mm_vd(va[kb], kf[kb], U[jI * NTD + D]);
+                    for (int kb = 0; kb < NKC; ++kb) U[j] = P::mm_vd(va[kb], kf[kb], U[j]);
                 }
             }
         }
-        wg_barrier();  // every read of H_c (sH) is done
+        wg_barrier();  // every read of H_c (sH), Qh/Kh and this chunk's v is done
+        const float e = sE[16 * I + l16];
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
-            if (I < NTM) {
-                const float e = sE[i];
-                if (e < 1.0f) {
+            const int D = gI + GI * j, i = 16 * I + l16;
+            if (D < NTD && e < 1.0f) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Hreg[j][r] = e * (Hreg[j][r] + U[j][r]);
+                for (int r = 0; r < 4; ++r) Hreg[j][r] = e * (Hreg[j][r] + U[j][r]);
+                if (!pass_a)
                     P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
-                }
             }
         }
+        if (pass_a) Eseg *= e;
     };
-    for (long c = 0; c < nC; c += 2) {
+    for (long c = c_begin; c < c_end; c += 2) {
         chunk(std::integral_constant<int, 0>{}, c);
-        if (c + 1 < nC) chunk(std::integral_constant<int, 1>{}, c + 1);
+        if (c + 1 < c_end) chunk(std::integral_constant<int, 1>{}, c + 1);
     }
 
-    if (H_out) {
+    if (pass_a) {
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
-            const int I = w + NW * (j / NTD), D = j % NTD, i = 16 * I + l16;
-            if (I < NTM)
+            const int D = gI + GI * j, i = 16 * I + l16;
+            if (D < NTD)
+                *reinterpret_cast<float4*>(sg.dH + (segrow + i) * Dv + d0 + 16 * D + 4 * q4) =
+                    make_float4(Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+        }
+        if (dtile == 0 && gI == 0 && q4 == 0) sg.dE[segrow + 16 * I + l16] = Eseg;
+    } else if (H_out && seg == sg.S - 1) {
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+            const int D = gI + GI * j, i = 16 * I + l16;
+            if (D < NTD)
                 *reinterpret_cast<float4*>(H_out + (bh * M + i) * Dv + d0 + 16 * D + 4 * q4) =
                     make_float4(Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
         }
@@ -676,83 +707,126 @@ __global__ void copy_state_kernel(const float* __restrict__ H0, float* __restric
 // ------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Chunk length the kernels run: the requested C, except fp32 inputs with M = 128, whose
-// C = 64 tiles do not fit in LDS and run as chunks of 32 (same result up to rounding).
-static int scan_chunk(int dtype, int M, int C) { return (dtype == RSM_F32 && M == 128 && C > 32) ? 32 : C; }
+// Chunk length the kernels run: the requested C, except M = 128, whose C = 64 tiles do not
+// fit in LDS and run as chunks of 32 (same result up to rounding).
+static int scan_chunk(int M, int C) { return (M == 128 && C > 32) ? 32 : C; }
+
+// Dv tile of a workgroup: the whole head up to 128 columns (bf16) / 64 (fp32), half that
+// for M = 128, so the fp32 state tile is at most 32 KB.
+static int pick_dt(int dtype, int M, int Dv) {
+    int cap = dtype == RSM_F32 ? 64 : 128;
+    if (M >= 128) cap /= 2;
+    return Dv < cap ? Dv : cap;
+}
+
+// Enough workgroups to fill the chip: segments per head so that heads x Dv tiles x
+// segments reaches 256, at least one chunk per segment.
+static void pick_segments(long heads_x_tiles, long nC, int& S, int& cps) {
+    long s = 1;
+    while (heads_x_tiles * s < 256 && s * 2 <= nC) s *= 2;
+    cps = int((nC + s - 1) / s);
+    S = nC > 0 ? int((nC + cps - 1) / cps) : 1;
+}
 
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K) {
-    (void)Dv;
-    C = scan_chunk(dtype, M, C);
+    C = scan_chunk(M, C);
     FwdLayout L{};
     L.chunk = C;
+    L.dt = pick_dt(dtype, M, Dv);
     L.n_chunks = (T + C - 1) / C;
     L.dense = K > compact_cap(M) ? 1 : 0;
+    pick_segments(B * Hh * (Dv / L.dt), L.n_chunks, L.S, L.cps);
     const size_t rows = size_t(B) * size_t(Hh) * size_t(L.n_chunks) * size_t(C);  // padded token-heads
+    if (rows == 0) return L;
+    size_t off = 0;
     if (L.dense) {
         L.ridx_off = 0;
         L.ralpha_off = 0;
-        L.total = align256(rows * size_t(M) * 4);
+        off = align256(rows * size_t(M) * 4);
     } else {
         L.ridx_off = 0;
         L.ralpha_off = align256(rows * size_t(K));
-        L.total = L.ralpha_off + align256(rows * size_t(K) * 4);
+        off = L.ralpha_off + align256(rows * size_t(K) * 4);
     }
-    if (rows == 0) L.total = 0;
+    const size_t segs = size_t(B) * size_t(Hh) * size_t(L.S - 1);
+    L.dh_off = off;
+    off += align256(segs * size_t(M) * size_t(Dv) * 4);
+    L.de_off = off;
+    off += align256(segs * size_t(M) * 4);
+    L.total = off;
     return L;
 }
 
-// Dv tile of the scan: 32 columns, 16 for M = 128 (LDS budget) or when Dv is 16.
-static int pick_dt(int M, int Dv) { return (M >= 128 || Dv % 32 != 0) ? 16 : 32; }
-
 template <typename T, int M, int C, int DT, bool DENSE>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
-                       int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
-                       hipStream_t s) {
-    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(B * Hh * (Dv / DT))), dim3(256), 0, s, q,
-                       k, v, H0, T_len, int(Hh), Dv, K, nC, ridx, ralpha, o, H_out);
+                       int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha, float* o,
+                       float* H_out, hipStream_t s) {
+    const long tiles = B * Hh * (Dv / DT);
+    if (sg.S > 1) {
+        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(tiles * (sg.S - 1))), dim3(512), 0,
+                           s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, 1, ridx, ralpha, o, H_out);
+        if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
+    }
+    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(tiles * sg.S)), dim3(512), 0, s, q, k,
+                       v, H0, T_len, int(Hh), Dv, K, sg, 0, ridx, ralpha, o, H_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
 template <typename T, int M, int C>
-static int dispatch_dt(bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh,
-                       int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o, float* H_out,
-                       hipStream_t s) {
-    if (pick_dt(M, Dv) == 32) {
-        if constexpr (M < 128) {
-            if (dense) return launch_scan<T, M, C, 32, true>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-            return launch_scan<T, M, C, 32, false>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        }
-        return RSM_ERR_UNSUPPORTED;
+static int dispatch_dt(int DT, bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len,
+                       long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha, float* o,
+                       float* H_out, hipStream_t s) {
+#define RSM_SCAN(DTV)                                                                                           \
+    return dense ? launch_scan<T, M, C, DTV, true>(q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s) \
+                 : launch_scan<T, M, C, DTV, false>(q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s)
+    constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);
+    switch (DT) {
+        case 16: RSM_SCAN(16);
+        case 32: RSM_SCAN(32);
+        case 64:
+            if constexpr (cap >= 64) { RSM_SCAN(64); }
+            break;
+        case 128:
+            if constexpr (cap >= 128) { RSM_SCAN(128); }
+            break;
     }
-    if (dense) return launch_scan<T, M, C, 16, true>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-    return launch_scan<T, M, C, 16, false>(q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+#undef RSM_SCAN
+    return RSM_ERR_UNSUPPORTED;
 }
 
 template <typename T, int M>
-static int dispatch_c(int C, bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len,
-                      long Hh, int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o,
-                      float* H_out, hipStream_t s) {
+static int dispatch_c(int C, int DT, bool dense, const T* q, const T* k, const T* v, const float* H0, long B,
+                      long T_len, long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha,
+                      float* o, float* H_out, hipStream_t s) {
     switch (C) {
-        case 16: return dispatch_dt<T, M, 16>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 32: return dispatch_dt<T, M, 32>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 16:
+            return dispatch_dt<T, M, 16>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
+        case 32:
+            return dispatch_dt<T, M, 32>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
         case 64:
-            if constexpr (sizeof(T) == 4 && M == 128) return RSM_ERR_UNSUPPORTED;
-            else return dispatch_dt<T, M, 64>(dense, q, k, v, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+            if constexpr (M < 128)
+                return dispatch_dt<T, M, 64>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
+                                             s);
+            break;
     }
     return RSM_ERR_UNSUPPORTED;
 }
 
 template <typename T>
-static int dispatch_m(int M, int C, bool dense, const void* q, const void* k, const void* v, const float* H0, long B,
-                      long T_len, long Hh, int Dv, int K, long nC, const uint8_t* ridx, const float* ralpha, float* o,
-                      float* H_out, hipStream_t s) {
+static int dispatch_m(int M, int C, int DT, bool dense, const void* q, const void* k, const void* v, const float* H0,
+                      long B, long T_len, long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx,
+                      const float* ralpha, float* o, float* H_out, hipStream_t s) {
     const T *qq = static_cast<const T*>(q), *kk = static_cast<const T*>(k), *vv = static_cast<const T*>(v);
     switch (M) {
-        case 16: return dispatch_c<T, 16>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 32: return dispatch_c<T, 32>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
-        case 64: return dispatch_c<T, 64>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+        case 16:
+            return dispatch_c<T, 16>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
+        case 32:
+            return dispatch_c<T, 32>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
+        case 64:
+            return dispatch_c<T, 64>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
         case 128:
-            return dispatch_c<T, 128>(C, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, nC, ridx, ralpha, o, H_out, s);
+            return dispatch_c<T, 128>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
+                                      s);
     }
     return RSM_ERR_UNSUPPORTED;
 }
@@ -770,17 +844,18 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
         return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
     }
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
-    C = L.chunk;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     uint8_t* ridx = ws + L.ridx_off;
     float* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
-    const long T_pad = L.n_chunks * C;
-    int st = route_fwd_launch(z, dtype, f, B, T, Hh, T_pad, M, K, L.dense, idx_out, ridx, ralpha, stream);
+    const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),
+                     reinterpret_cast<float*>(ws + L.de_off)};
+    int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.dense, idx_out, ridx, ralpha,
+                              stream);
     if (st != RSM_OK) return st;
     if (dtype == RSM_F32)
-        return dispatch_m<float>(M, C, L.dense, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out,
+        return dispatch_m<float>(M, L.chunk, L.dt, L.dense, q, k, v, H0, B, T, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
                                  stream);
-    return dispatch_m<bf16_t>(M, C, L.dense, q, k, v, H0, B, T, Hh, Dv, K, L.n_chunks, ridx, ralpha, o, H_out,
+    return dispatch_m<bf16_t>(M, L.chunk, L.dt, L.dense, q, k, v, H0, B, T, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
                               stream);
 }
 

@@ -19,12 +19,18 @@ int decode_step_launch(const void* q, const void* k, const void* z, const void* 
 
 // Workspace of the chunked forward: the route of every token-head in (batch*head, padded
 // token) order, either compact (slot uint8 + alpha fp32 per selected slot) or dense (alpha
-// fp32 for every slot, used when K is a large fraction of M); byte offsets and total.
+// fp32 for every slot, used when K is a large fraction of M), then the state and decay
+// product of every sequence segment but the last; byte offsets and total.
 struct FwdLayout {
-    size_t ridx_off, ralpha_off, total;
+    size_t ridx_off, ralpha_off;  // route
+    size_t dh_off, de_off;        // per-segment states and decay products (S > 1)
+    size_t total;
     long n_chunks;
     int dense;  // route as dense alphas [..][M] (K large) instead of (slot, alpha) lists
     int chunk;  // chunk length the kernels run
+    int dt;     // Dv columns per workgroup
+    int S;      // sequence segments per head
+    int cps;    // chunks per segment
 };
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
 
