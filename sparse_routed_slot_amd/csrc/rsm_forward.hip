@@ -17,14 +17,15 @@
 //
 // Kernels:
 //  * route (rsm_route.hip, fully parallel): exact top-K per token-head and alpha, written as
-//    a compact list (slot, alpha) per token, or as dense alphas when K is a large fraction
-//    of M -- the only intermediate in memory.
+//    a selection bit mask plus the alphas of the selected slots -- the only intermediate in
+//    memory.
 //  * fwd_scan (one workgroup per (batch, head, Dv tile)): walks the chunks in order with the
 //    fp32 state tile in registers.  The chunk's raw q, k, v tiles and its route arrive in
-//    LDS by direct global->LDS loads issued while the previous chunk computes.  Per chunk it
-//    scatters the alphas into a dense tile in LDS, forms the decay products E by prefix
-//    products along the chunk, builds Qh and Kh in LDS, runs the three contractions on
-//    16x16 MFMA tiles, writes o, and updates the state.  Rows of slots untouched in a chunk
+//    LDS by direct global->LDS loads issued while the previous chunk computes.  Per chunk
+//    each lane takes one token and each wave a group of slots: the lane gathers its alphas
+//    from the route, the decay products E come from a product scan across the wave's lanes,
+//    and the lane writes its rows of Qh and Kh.  Then the three contractions run on 16x16
+//    MFMA tiles, o is written, and the state is updated.  Rows of slots untouched in a chunk
 //    (E_last == 1) are not written, so they keep their exact bits.
 //
 // Overflow guard: 1/E grows with the decay accumulated in a chunk.  On the factored path each
@@ -93,9 +94,17 @@ template <> struct Pol<float> {
     __device__ static __forceinline__ void put4(E* arr, int ps, int i, float a, float b, float c, float d) {
         *reinterpret_cast<float4*>(arr + i) = make_float4(a, b, c, d);
     }
-    // EVT = 4 consecutive values (16-byte aligned)
-    __device__ static __forceinline__ void put_vec(E* arr, int ps, int i, const float* x) {
-        *reinterpret_cast<float4*>(arr + i) = make_float4(x[0], x[1], x[2], x[3]);
+    // N consecutive values (N*4 bytes aligned to min(16, N*4))
+    template <int N>
+    __device__ static __forceinline__ void put_row(E* arr, int ps, int i, const float (&x)[N]) {
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int g = 0; g < N / 4; ++g)
+                *reinterpret_cast<float4*>(arr + (i + 4 * g)) = make_float4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+        } else {
+#pragma unroll
+            for (int g = 0; g < N / 2; ++g) *reinterpret_cast<float2*>(arr + (i + 2 * g)) = make_float2(x[2 * g], x[2 * g + 1]);
+        }
     }
     template <int NT>
     __device__ static __forceinline__ dfrag pack_perm(const floatx4 (&st)[NT], int kb) {
@@ -153,12 +162,27 @@ template <> struct Pol<bf16_t> {
         *reinterpret_cast<uint2*>(arr + i) = make_uint2(h0, h1);
         *reinterpret_cast<uint2*>(arr + (ps + i)) = make_uint2(l0, l1);
     }
-    __device__ static __forceinline__ void put_vec(E* arr, int ps, int i, const float* x) {
-        uint32_t l0, l1, l2, l3;
-        const uint32_t h0 = split2(x[0], x[1], l0), h1 = split2(x[2], x[3], l1);
-        const uint32_t h2 = split2(x[4], x[5], l2), h3 = split2(x[6], x[7], l3);
-        *reinterpret_cast<uint4*>(arr + i) = make_uint4(h0, h1, h2, h3);
-        *reinterpret_cast<uint4*>(arr + (ps + i)) = make_uint4(l0, l1, l2, l3);
+    // N consecutive values as hi / lo planes (N*2 bytes aligned to min(16, N*2))
+    template <int N>
+    __device__ static __forceinline__ void put_row(E* arr, int ps, int i, const float (&x)[N]) {
+        static_assert(N % 2 == 0, "pairs of bf16");
+        uint32_t hi[N / 2], lo[N / 2];
+#pragma unroll
+        for (int p = 0; p < N / 2; ++p) hi[p] = split2(x[2 * p], x[2 * p + 1], lo[p]);
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int g = 0; g < N / 8; ++g) {
+                *reinterpret_cast<uint4*>(arr + (i + 8 * g)) = make_uint4(hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3]);
+                *reinterpret_cast<uint4*>(arr + (ps + i + 8 * g)) =
+                    make_uint4(lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3]);
+            }
+        } else if constexpr (N == 4) {
+            *reinterpret_cast<uint2*>(arr + i) = make_uint2(hi[0], hi[1]);
+            *reinterpret_cast<uint2*>(arr + (ps + i)) = make_uint2(lo[0], lo[1]);
+        } else {
+            *reinterpret_cast<uint32_t*>(arr + i) = hi[0];
+            *reinterpret_cast<uint32_t*>(arr + (ps + i)) = lo[0];
+        }
     }
     template <int NT>
     __device__ static __forceinline__ dfrag pack_perm(const floatx4 (&st)[NT], int kb) {
@@ -236,8 +260,63 @@ __device__ __forceinline__ void wg_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Compact route capacity: K up to KC uses (slot, alpha) lists, larger K dense alphas.
-constexpr int compact_cap(int M) { return M / 2 < 32 ? M / 2 : 32; }
+// Inclusive product scan across the 64 lanes of a wave (lane order): DPP row shifts by 1, 2,
+// 4, 8 within rows of 16 lanes, then row broadcasts of lane 15 and lane 31.  Lanes without a
+// source lane in a step multiply by 1 (the "old" operand of the DPP move).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float scan_mul_step(float x) {
+    const int y = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL, ROWMASK, 0xF, false);
+    return x * __int_as_float(y);
+}
+__device__ __forceinline__ float wave_scan_mul(float x) {
+    x = scan_mul_step<0x111, 0xF>(x);  // row_shr:1
+    x = scan_mul_step<0x112, 0xF>(x);  // row_shr:2
+    x = scan_mul_step<0x114, 0xF>(x);  // row_shr:4
+    x = scan_mul_step<0x118, 0xF>(x);  // row_shr:8
+    x = scan_mul_step<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = scan_mul_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// N consecutive input elements (N*sizeof(T) a multiple of 4 bytes, aligned) -> fp32
+template <int N>
+__device__ __forceinline__ void load_row(const bf16_t* arr, int off, float (&x)[N]) {
+    static_assert(N % 2 == 0, "pairs of bf16");
+    uint32_t wds[N / 2];
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int g = 0; g < N / 8; ++g) {
+            const uint4 u = *reinterpret_cast<const uint4*>(arr + (off + 8 * g));
+            wds[4 * g] = u.x; wds[4 * g + 1] = u.y; wds[4 * g + 2] = u.z; wds[4 * g + 3] = u.w;
+        }
+    } else if constexpr (N == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(arr + off);
+        wds[0] = u.x; wds[1] = u.y;
+    } else {
+        wds[0] = *reinterpret_cast<const uint32_t*>(arr + off);
+    }
+#pragma unroll
+    for (int p = 0; p < N / 2; ++p) {
+        x[2 * p] = __uint_as_float(wds[p] << 16);
+        x[2 * p + 1] = __uint_as_float(wds[p] & 0xFFFF0000u);
+    }
+}
+template <int N>
+__device__ __forceinline__ void load_row(const float* arr, int off, float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int g = 0; g < N / 4; ++g) {
+            const float4 u = *reinterpret_cast<const float4*>(arr + (off + 4 * g));
+            x[4 * g] = u.x; x[4 * g + 1] = u.y; x[4 * g + 2] = u.z; x[4 * g + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < N / 2; ++g) {
+            const float2 u = *reinterpret_cast<const float2*>(arr + (off + 2 * g));
+            x[2 * g] = u.x; x[2 * g + 1] = u.y;
+        }
+    }
+}
 
 // ------------------------------------------------------------------------------------
 // Sequence segments.  A head's chunks are cut into S consecutive segments so that a launch
@@ -259,18 +338,18 @@ struct SegArgs {
 // ------------------------------------------------------------------------------------
 // Chunk scan: one workgroup (8 waves) per (b, h, Dv tile of DT columns, segment); it walks
 // the segment's chunks in order with the fp32 state tile in registers.
-// DENSE: the route arrives as dense alphas [C][M] instead of (slot, alpha) lists.
 // pass_a: pass A of the segment split (no Qh, no outputs; writes dH, dE).
 //
 // Wave roles (w = 0..7, all uniform):
+//  * decay products, Qh, Kh: lane = token of the chunk, wave w = slots w*SPW .. w*SPW+SPW-1;
 //  * chunk-row tile Tt of S^T and O^T: waves w and w + NTC*g share Tt; odd groups take the
 //    tiles in reverse so that the two waves of a SIMD (w, w+4) get a cheap and a costly tile;
 //  * slot tile I = w % NTM of U^T and of the state, column tiles gI, gI + GI, ...
 // ------------------------------------------------------------------------------------
-template <typename T, int M, int C, int DT, bool DENSE>
+template <typename T, int M, int C, int DT>
 __global__ __launch_bounds__(512) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
-    long T_len, int Hh, int Dv, int K, SegArgs sg, int pass_a, const uint8_t* __restrict__ ridx,
+    long T_len, int Hh, int Dv, int K, SegArgs sg, int pass_a, const unsigned long long* __restrict__ rmask,
     const float* __restrict__ ralpha, float* __restrict__ o, float* __restrict__ H_out) {
     typedef Pol<T> P;
     typedef typename P::E E;
@@ -289,16 +368,14 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int NOD = (NTD + GT - 1) / GT;   // output column tiles per wave
     constexpr int GI = NW / NTM;               // waves per slot tile
     constexpr int UPW = (NTD + GI - 1) / GI;   // state tiles per wave
-    constexpr int NPART = NT / M < C ? NT / M : C;  // token parts of the decay products
-    constexpr int TPP = C / NPART;
-    constexpr int KC = compact_cap(M);
-    constexpr int RPT = NT / C;                // threads per token for the compact route
+    constexpr int SPW = M / NW;                // slots per wave in the decay-product pass
+    constexpr int MW = (M + 63) / 64;          // 64-bit words of a token's selection mask
     constexpr int psQ = CP * QP + 8;           // plane stride of Qh / Kh
     constexpr int oK = NPL * psQ;              // Kh planes start here
     constexpr int psH = MP * HP;               // plane stride of the state copy
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int SZHF = M * DT * 4 / int(sizeof(E));
-    static_assert(NW % NTC == 0 && NW % NTM == 0 && NT % C == 0, "tile split");
+    static_assert(NW % NTC == 0 && NW % NTM == 0 && SPW >= 2 && SPW <= 16 && C <= 64, "tile split");
 
     // LDS.  Raw inputs land by direct loads (tile arrays padded to 1 KB); every array is a
     // separate object so the compiler can tell the direct loads from the other accesses.
@@ -306,13 +383,11 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     __shared__ __align__(16) T rk[pad1k(C * M * int(sizeof(T))) / int(sizeof(T))];
     __shared__ __align__(16) T rv0[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, even chunks
     __shared__ __align__(16) T rv1[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, odd chunks
-    __shared__ __align__(16) float rA[DENSE ? 4 : pad1k(C * KC * 4) / 4];
-    __shared__ __align__(16) uint8_t rI[DENSE ? 16 : pad1k(C * KC)];
-    __shared__ __align__(16) float sA[pad1k(C * M * 4) / 4];        // exact alphas of the chunk
+    __shared__ __align__(16) unsigned long long rMask[pad1k(C * MW * 8) / 8];  // selection masks
+    __shared__ __align__(16) float rA[pad1k(C * M * 4) / 4];  // alpha lists; exact path: dense alphas [C][M]
     __shared__ __align__(16) E sQK[SZQK > SZHF ? SZQK : SZHF];      // Qh planes, then Kh planes
     __shared__ __align__(16) E sH[NPL * psH];                       // state copy, row-major [i][d]
-    __shared__ float sTot[NPART * M];
-    __shared__ float sE[M];
+    __shared__ __align__(16) float sE[M];
     __shared__ int sFlag[NW];
     float* sHf = reinterpret_cast<float*>(sQK);  // exact path: fp32 state [M][DT]
 
@@ -339,8 +414,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     const int gT = w / NTC;
     const int Tt = (gT & 1) ? NTC - 1 - w % NTC : w % NTC;
     const int I = w % NTM, gI = w / NTM;
-    const int rt = tid / RPT, rsub = tid % RPT;     // compact route entries: token, first entry
-    const int pslot = tid % M, ppart = tid / M;     // decay products: slot, token part
+    const int s0 = w * SPW;                         // first slot of this wave's decay products
     const long rstride = long(Hh);                  // rows between consecutive tokens of one head
     const long segrow = (bh * (sg.S - 1) + seg) * M;  // row of this segment in dH / dE
 
@@ -373,19 +447,12 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         });
     };
     auto issue_route = [&](long c) {
-        if (DENSE) {
-            const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * M);
-            dma_tile<NW>(sA, int(sizeof(sA)), w, lane,
-                         [&](int off) { return static_cast<const void*>(ab + min(off, C * M * 4 - 16)); });
-        } else {
-            const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * K);
-            const char* ib = reinterpret_cast<const char*>(ridx + (bh * T_pad + c * C) * K);
-            const int na = C * K * 4, ni = C * K;
-            dma_tile<NW>(rA, pad1k(na), w, lane,
-                         [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); });
-            dma_tile<NW>(rI, pad1k(ni), w, lane,
-                         [&](int off) { return static_cast<const void*>(ib + min(off, ni - 16)); });
-        }
+        const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * K);
+        const char* mb = reinterpret_cast<const char*>(rmask + (bh * T_pad + c * C) * MW);
+        const int na = C * K * 4, nm = C * MW * 8;
+        dma_tile<NW>(rA, pad1k(na), w, lane, [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); });
+        dma_tile<NW>(rMask, pad1k(nm), w, lane,
+                     [&](int off) { return static_cast<const void*>(mb + min(off, nm - 16)); });
     };
 
     // ---- start state in registers: tile j holds H[16*I + l16][16*D + 4*q4 + r], D = gI + GI*j.
@@ -428,8 +495,6 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         issue_v(c_begin, rv0);
         issue_route(c_begin);
     }
-    if (!DENSE)
-        for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
 
     // One chunk.  CUR selects the v buffer statically (even chunks of the segment rv0, odd
     // rv1) so the compiler can tell the in-flight loads of the next chunk's v from this
@@ -443,61 +508,63 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         wg_barrier();                   // ... and every other wave's
         if (c + 1 < c_end) issue_v(c + 1, CUR ? rv0 : rv1);
 
-        // ---- compact route: scatter the exact alphas into the dense tile (1 elsewhere)
-        if (!DENSE) {
-            if (rt < nvalid) {
-#pragma unroll
-                for (int j = 0; j < (KC + RPT - 1) / RPT; ++j) {
-                    const int n = rsub + RPT * j;
-                    if (n < K) sA[rt * M + rI[rt * K + n]] = rA[rt * K + n];
+        // ---- decay products, Qh = q o E and Kh = k (1 - alpha) / E (0 where alpha = 1).
+        // Lane = token t of the chunk, this wave's slots s0 .. s0 + SPW - 1.  The lane gathers
+        // its alphas through the token's selection mask (position in the alpha list = number
+        // of selected slots below); E is an inclusive product scan across the lanes of the
+        // clamped alphas.  Tokens past the sequence end have alpha = 1.
+        float al[SPW], Ev[SPW];
+        {
+            const int tc = lane < C ? lane : C - 1;
+            unsigned long long word = 0ull;
+            int base = 0;
+            if (lane < nvalid) {
+                const unsigned long long w0 = rMask[tc * MW];
+                if (MW == 1 || s0 < 64) {
+                    word = w0;
+                    base = __popcll(w0 & ((1ull << (s0 & 63)) - 1ull));
+                } else {
+                    word = rMask[tc * MW + 1];
+                    base = __popcll(w0) + __popcll(word & ((1ull << (s0 & 63)) - 1ull));
                 }
             }
-            wg_barrier();
-        }
-
-        // ---- decay products: thread (slot pslot, part ppart) runs over its TPP tokens with
-        // the clamped alphas; the parts' products are combined through LDS
-        float Eloc[TPP], Aloc[TPP];
-        if (ppart < NPART) {
-            float run = 1.0f;
+            const uint32_t g = uint32_t(word >> (s0 & 63));
+            int idx = base;
 #pragma unroll
-            for (int tt = 0; tt < TPP; ++tt) {
-                const int t = ppart * TPP + tt;
-                const float a = t < nvalid ? sA[t * M + pslot] : 1.0f;
-                Aloc[tt] = a;
-                run *= fmaxf(a, kAlphaMin);
-                Eloc[tt] = run;
+            for (int j = 0; j < SPW; ++j) {
+                const bool sel = (g >> j) & 1u;
+                const float a = rA[tc * K + (idx < K ? idx : K - 1)];
+                al[j] = sel ? a : 1.0f;
+                idx += sel ? 1 : 0;
             }
-            sTot[ppart * M + pslot] = run;
         }
-        wg_barrier();
-
-        // ---- E, and in the same pass Qh = q o E and Kh = k (1 - alpha) / E (0 where alpha = 1)
         int bad = 0;
-        if (ppart < NPART) {
-            float pre = 1.0f, last = 1.0f;
 #pragma unroll
-            for (int p = 0; p < NPART; ++p) {
-                const float tp = sTot[p * M + pslot];
-                pre = p < ppart ? pre * tp : pre;
-                last *= tp;
-            }
-#pragma unroll
-            for (int tt = 0; tt < TPP; ++tt) {
-                const int t = ppart * TPP + tt;
-                const float ev = pre * Eloc[tt];
-                if (!pass_a) P::put(sQK, psQ, t * QP + pslot, Elem<T>::load(rq, t * M + pslot) * ev);
-                const float a = fmaxf(Aloc[tt], kAlphaMin);
-                const float kh =
-                    a < 1.0f ? Elem<T>::load(rk, t * M + pslot) * (1.0f - a) * __builtin_amdgcn_rcpf(ev) : 0.0f;
-                P::put(sQK, psQ, oK + t * QP + pslot, kh);
-            }
-            if (ppart == 0) sE[pslot] = last;
-            bad = !(last >= kSafeMin);
+        for (int j = 0; j < SPW; ++j) {
+            Ev[j] = wave_scan_mul(fmaxf(al[j], kAlphaMin));
+            const float el = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ev[j]), 63));
+            bad |= !(el >= kSafeMin);
         }
-        {
-            const bool wave_bad = __ballot(bad) != 0;
-            if (lane == 0) sFlag[w] = wave_bad;
+        if (lane == 63) {  // E at the chunk end, per slot
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) sE[s0 + j] = Ev[j];
+        }
+        if (lane == 0) sFlag[w] = bad;
+        if (lane < C) {
+            float x[SPW];
+            load_row<SPW>(rk, lane * M + s0, x);
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                const float a = fmaxf(al[j], kAlphaMin);
+                x[j] = a < 1.0f ? x[j] * (1.0f - a) * __builtin_amdgcn_rcpf(Ev[j]) : 0.0f;
+            }
+            P::template put_row<SPW>(sQK, psQ, oK + lane * QP + s0, x);
+            if (!pass_a) {
+                load_row<SPW>(rq, lane * M + s0, x);
+#pragma unroll
+                for (int j = 0; j < SPW; ++j) x[j] *= Ev[j];
+                P::template put_row<SPW>(sQK, psQ, lane * QP + s0, x);
+            }
         }
         wg_barrier();
         int unsafe = 0;
@@ -505,7 +572,14 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         for (int i = 0; i < NW; ++i) unsafe |= sFlag[i];
 
         if (unsafe) {
-            // ---- exact token-by-token recurrence with the exact alphas, on an fp32 copy
+            // ---- exact token-by-token recurrence with the exact alphas, on an fp32 copy.
+            // Dense exact alphas [C][M] go where the alpha lists were (all lists are read).
+            if (lane < C) {
+                float x[SPW];
+#pragma unroll
+                for (int j = 0; j < SPW; ++j) x[j] = al[j];
+                Pol<float>::template put_row<SPW>(rA, 0, lane * M + s0, x);
+            }
 #pragma unroll
             for (int j = 0; j < UPW; ++j) {
                 const int D = gI + GI * j, i = 16 * I + l16;
@@ -518,7 +592,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             for (int tt = 0; tt < nvalid; ++tt) {
                 for (int e = tid; e < M * DT; e += NT) {
                     const int i = e / DT, dd = e % DT;
-                    const float a = sA[tt * M + i];
+                    const float a = rA[tt * M + i];
                     if (a != 1.0f) {
                         const float wk = (1.0f - a) * Elem<T>::load(rk, tt * M + i);
                         sHf[e] = fmaf(a, sHf[e], wk * Elem<T>::load(rvc, tt * DT + dd));
@@ -534,7 +608,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             }
             if (tid < M) {  // decay product of the chunk with the exact alphas
                 float e = 1.0f;
-                for (int tt = 0; tt < nvalid; ++tt) e *= sA[tt * M + tid];
+                for (int tt = 0; tt < nvalid; ++tt) e *= rA[tt * M + tid];
                 sE[tid] = e;
             }
 #pragma unroll
@@ -558,8 +632,6 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             } else {
                 Eseg *= sE[16 * I + l16];
             }
-            if (!DENSE)
-                for (int i = tid; i < C * M; i += NT) sA[i] = 1.0f;
             if (c + 1 < c_end) {
                 issue_qk(c + 1);
                 issue_route(c + 1);
@@ -567,10 +639,6 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             return;
         }
 
-        if (!DENSE)  // ready for the next chunk's scatter
-            for_each_tid<C * M / 4, NT>(tid, [&](int i) {
-                *reinterpret_cast<float4*>(sA + 4 * i) = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            });
         if (c + 1 < c_end) {
             issue_qk(c + 1);
             issue_route(c + 1);
@@ -734,20 +802,15 @@ FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int 
     L.chunk = C;
     L.dt = pick_dt(dtype, M, Dv);
     L.n_chunks = (T + C - 1) / C;
-    L.dense = K > compact_cap(M) ? 1 : 0;
     pick_segments(B * Hh * (Dv / L.dt), L.n_chunks, L.S, L.cps);
     const size_t rows = size_t(B) * size_t(Hh) * size_t(L.n_chunks) * size_t(C);  // padded token-heads
     if (rows == 0) return L;
+    const size_t mw = size_t(M + 63) / 64;
     size_t off = 0;
-    if (L.dense) {
-        L.ridx_off = 0;
-        L.ralpha_off = 0;
-        off = align256(rows * size_t(M) * 4);
-    } else {
-        L.ridx_off = 0;
-        L.ralpha_off = align256(rows * size_t(K));
-        off = L.ralpha_off + align256(rows * size_t(K) * 4);
-    }
+    L.rmask_off = off;
+    off += align256(rows * mw * 8);
+    L.ralpha_off = off;
+    off += align256(rows * size_t(K) * 4);
     const size_t segs = size_t(B) * size_t(Hh) * size_t(L.S - 1);
     L.dh_off = off;
     off += align256(segs * size_t(M) * size_t(Dv) * 4);
@@ -757,28 +820,38 @@ FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int 
     return L;
 }
 
-template <typename T, int M, int C, int DT, bool DENSE>
+template <typename T, int M, int C, int DT>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
-                       int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha, float* o,
+                       int K, const SegArgs& sg, const unsigned long long* rmask, const float* ralpha, float* o,
                        float* H_out, hipStream_t s) {
     const long tiles = B * Hh * (Dv / DT);
     if (sg.S > 1) {
-        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(tiles * (sg.S - 1))), dim3(512), 0,
-                           s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, 1, ridx, ralpha, o, H_out);
+        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT>), dim3(unsigned(tiles * (sg.S - 1))), dim3(512), 0, s, q, k,
+                           v, H0, T_len, int(Hh), Dv, K, sg, 1, rmask, ralpha, o, H_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
     }
-    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, DENSE>), dim3(unsigned(tiles * sg.S)), dim3(512), 0, s, q, k,
-                       v, H0, T_len, int(Hh), Dv, K, sg, 0, ridx, ralpha, o, H_out);
+    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT>), dim3(unsigned(tiles * sg.S)), dim3(512), 0, s, q, k, v, H0,
+                       T_len, int(Hh), Dv, K, sg, 0, rmask, ralpha, o, H_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
+struct ScanArgs {
+    const void *q, *k, *v;
+    const float* H0;
+    long B, T_len, Hh;
+    int Dv, K;
+    SegArgs sg;
+    const unsigned long long* rmask;
+    const float* ralpha;
+    float *o, *H_out;
+    hipStream_t s;
+};
+
 template <typename T, int M, int C>
-static int dispatch_dt(int DT, bool dense, const T* q, const T* k, const T* v, const float* H0, long B, long T_len,
-                       long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha, float* o,
-                       float* H_out, hipStream_t s) {
-#define RSM_SCAN(DTV)                                                                                           \
-    return dense ? launch_scan<T, M, C, DTV, true>(q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s) \
-                 : launch_scan<T, M, C, DTV, false>(q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s)
+static int dispatch_dt(int DT, const ScanArgs& a) {
+    const T *q = static_cast<const T*>(a.q), *k = static_cast<const T*>(a.k), *v = static_cast<const T*>(a.v);
+#define RSM_SCAN(DTV) \
+    return launch_scan<T, M, C, DTV>(q, k, v, a.H0, a.B, a.T_len, a.Hh, a.Dv, a.K, a.sg, a.rmask, a.ralpha, a.o, a.H_out, a.s)
     constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);
     switch (DT) {
         case 16: RSM_SCAN(16);
@@ -795,38 +868,24 @@ static int dispatch_dt(int DT, bool dense, const T* q, const T* k, const T* v, c
 }
 
 template <typename T, int M>
-static int dispatch_c(int C, int DT, bool dense, const T* q, const T* k, const T* v, const float* H0, long B,
-                      long T_len, long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx, const float* ralpha,
-                      float* o, float* H_out, hipStream_t s) {
+static int dispatch_c(int C, int DT, const ScanArgs& a) {
     switch (C) {
-        case 16:
-            return dispatch_dt<T, M, 16>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
-        case 32:
-            return dispatch_dt<T, M, 32>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
+        case 16: return dispatch_dt<T, M, 16>(DT, a);
+        case 32: return dispatch_dt<T, M, 32>(DT, a);
         case 64:
-            if constexpr (M < 128)
-                return dispatch_dt<T, M, 64>(DT, dense, q, k, v, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
-                                             s);
+            if constexpr (M < 128) return dispatch_dt<T, M, 64>(DT, a);
             break;
     }
     return RSM_ERR_UNSUPPORTED;
 }
 
 template <typename T>
-static int dispatch_m(int M, int C, int DT, bool dense, const void* q, const void* k, const void* v, const float* H0,
-                      long B, long T_len, long Hh, int Dv, int K, const SegArgs& sg, const uint8_t* ridx,
-                      const float* ralpha, float* o, float* H_out, hipStream_t s) {
-    const T *qq = static_cast<const T*>(q), *kk = static_cast<const T*>(k), *vv = static_cast<const T*>(v);
+static int dispatch_m(int M, int C, int DT, const ScanArgs& a) {
     switch (M) {
-        case 16:
-            return dispatch_c<T, 16>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
-        case 32:
-            return dispatch_c<T, 32>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
-        case 64:
-            return dispatch_c<T, 64>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out, s);
-        case 128:
-            return dispatch_c<T, 128>(C, DT, dense, qq, kk, vv, H0, B, T_len, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
-                                      s);
+        case 16: return dispatch_c<T, 16>(C, DT, a);
+        case 32: return dispatch_c<T, 32>(C, DT, a);
+        case 64: return dispatch_c<T, 64>(C, DT, a);
+        case 128: return dispatch_c<T, 128>(C, DT, a);
     }
     return RSM_ERR_UNSUPPORTED;
 }
@@ -845,18 +904,15 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
     }
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    uint8_t* ridx = ws + L.ridx_off;
-    float* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
+    auto* rmask = reinterpret_cast<unsigned long long*>(ws + L.rmask_off);
+    auto* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
     const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),
                      reinterpret_cast<float*>(ws + L.de_off)};
-    int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.dense, idx_out, ridx, ralpha,
-                              stream);
+    int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, idx_out, rmask, ralpha, stream);
     if (st != RSM_OK) return st;
-    if (dtype == RSM_F32)
-        return dispatch_m<float>(M, L.chunk, L.dt, L.dense, q, k, v, H0, B, T, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
-                                 stream);
-    return dispatch_m<bf16_t>(M, L.chunk, L.dt, L.dense, q, k, v, H0, B, T, Hh, Dv, K, sg, ridx, ralpha, o, H_out,
-                              stream);
+    const ScanArgs a{q, k, v, H0, B, T, Hh, Dv, K, sg, rmask, ralpha, o, H_out, stream};
+    if (dtype == RSM_F32) return dispatch_m<float>(M, L.chunk, L.dt, a);
+    return dispatch_m<bf16_t>(M, L.chunk, L.dt, a);
 }
 
 }  // namespace rsm

@@ -18,15 +18,14 @@ int decode_step_launch(const void* q, const void* k, const void* z, const void* 
                        int32_t* idx_out, hipStream_t stream);
 
 // Workspace of the chunked forward: the route of every token-head in (batch*head, padded
-// token) order, either compact (slot uint8 + alpha fp32 per selected slot) or dense (alpha
-// fp32 for every slot, used when K is a large fraction of M), then the state and decay
-// product of every sequence segment but the last; byte offsets and total.
+// token) order -- a selection bit mask (uint64 words) and the alphas of the selected slots
+// (fp32, ascending slot order) -- then the state and decay product of every sequence
+// segment but the last; byte offsets and total.
 struct FwdLayout {
-    size_t ridx_off, ralpha_off;  // route
-    size_t dh_off, de_off;        // per-segment states and decay products (S > 1)
+    size_t rmask_off, ralpha_off;  // route
+    size_t dh_off, de_off;         // per-segment states and decay products (S > 1)
     size_t total;
     long n_chunks;
-    int dense;  // route as dense alphas [..][M] (K large) instead of (slot, alpha) lists
     int chunk;  // chunk length the kernels run
     int dt;     // Dv columns per workgroup
     int S;      // sequence segments per head
@@ -35,7 +34,7 @@ struct FwdLayout {
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int dense_out, int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream);
+                     int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream);
 
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,

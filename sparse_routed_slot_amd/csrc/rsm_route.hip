@@ -8,9 +8,10 @@
 // from a bitonic sort of distinct packed keys (rsm_device.h).  Selected slots are
 // collected in ascending slot order through per-lane LDS lists, then scored:
 //  * public router: idx (int32) and score = sigmoid(z) per selected slot;
-//  * forward router: the compact per-token route the chunked forward consumes -- slot
-//    (uint8) and alpha = exp(s*f) (fp32, exact: 0 for f = -inf, 1 when s*f == 0) -- in
-//    (batch*head, token) order, plus the optional int32 idx output in (b, t, h) order.
+//  * forward router: the per-token route the chunked forward consumes -- a selection bit
+//    mask over the M slots and alpha = exp(s*f) of the selected slots in ascending slot
+//    order (fp32, exact: 0 for f = -inf, 1 when s*f == 0) -- in (batch*head, token) order,
+//    plus the optional int32 idx output in (b, t, h) order.
 #include "rsm_device.h"
 #include "rsm_launch.h"
 
@@ -52,14 +53,14 @@ template <int M> struct RowRegs<float, M> {
 
 // kFwd = false: public router (idx int32 [row][K], score [row][K] or NULL).
 // kFwd = true : forward router, rows written in (b*Hh + h, t) order with T_pad tokens per
-//               head: compact form (dense == 0) ridx uint8 / ralpha fp32 [..][K] in ascending
-//               slot order, or dense form (dense == 1) ralpha fp32 [..][M] with alpha for
-//               every slot (1 for unselected slots); idx int32 [row][K] or NULL either way.
+//               head: rmask uint64 [..][MW] (bit i%64 of word i/64 set iff slot i is
+//               selected, MW = ceil(M/64)) and ralpha fp32 [..][K] in ascending slot order;
+//               idx int32 [row][K] or NULL.
 template <typename T, int M, bool kFwd>
 __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z, const float* __restrict__ f,
                                                         long n_rows, long T_len, int Hh, long T_pad, int K,
-                                                        int dense_out, int32_t* __restrict__ idx,
-                                                        float* __restrict__ score, uint8_t* __restrict__ ridx,
+                                                        int32_t* __restrict__ idx, float* __restrict__ score,
+                                                        unsigned long long* __restrict__ rmask,
                                                         float* __restrict__ ralpha) {
     typedef typename RowKey<T>::type U;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -77,31 +78,28 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
     for (int i = 0; i < M; ++i) v[i] = x.val(i);
     U th = 0;
     if (!all) th = row_threshold<T, M>(v, K);
-    long dst = row * K;
-    float ft = 0.0f;
+    const long dst = row * K;
     if (kFwd) {
+        constexpr int MW = (M + 63) / 64;
         const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
-        dst = ((b * Hh + h) * T_pad + t) * (dense_out ? M : K);
-        ft = f[row];
-    }
-    if (kFwd && dense_out) {
+        const long orow = (b * Hh + h) * T_pad + t;
+        const float ft = f[row];
+        unsigned long long mk[MW];
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
         int n = 0;
 #pragma unroll
-        for (int i0 = 0; i0 < M; i0 += 4) {
-            float a4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = i0 + e;
-                a4[e] = 1.0f;
-                if (all || RowKey<T>::make(v[i], i) >= th) {
-                    const float s = sigmoidf_dev(v[i]);
-                    if (s > 0.0f) a4[e] = __expf(s * ft);
-                    if (idx) idx[row * K + n] = i;
-                    ++n;
-                }
+        for (int i = 0; i < M; ++i) {
+            if (all || RowKey<T>::make(v[i], i) >= th) {
+                mk[i >> 6] |= 1ull << (i & 63);
+                const float s = sigmoidf_dev(v[i]);
+                ralpha[orow * K + n] = s > 0.0f ? __expf(s * ft) : 1.0f;
+                if (idx) idx[dst + n] = i;
+                ++n;
             }
-            *reinterpret_cast<float4*>(ralpha + dst + i0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
         }
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
         return;
     }
     if (!all) {
@@ -118,28 +116,20 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
     for (int n = 0; n < K; ++n) {
         const int i = all ? n : s_slot[n * 64 + lane];
         const float zi = all ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane];
-        const float s = sigmoidf_dev(zi);
-        if (kFwd) {
-            ridx[dst + n] = uint8_t(i);
-            ralpha[dst + n] = s > 0.0f ? __expf(s * ft) : 1.0f;
-            if (idx) idx[row * K + n] = i;
-        } else {
-            idx[dst + n] = i;
-            if (score) score[dst + n] = s;
-        }
+        idx[dst + n] = i;
+        if (score) score[dst + n] = sigmoidf_dev(zi);
     }
 }
 
 template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K,
-                       int dense_out, int32_t* idx, float* score, uint8_t* ridx, float* ralpha,
-                       hipStream_t stream) {
+                       int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
     const dim3 grid(unsigned((n_rows + 63) / 64)), block(64);
-    const size_t lds = (dense_out || K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane lists, compact form
+    const size_t lds = (kFwd || K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane slot lists (public router)
 #define RSM_ROUTE_LAUNCH(MM)                                                                                    \
     hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, T_pad, \
-                       K, dense_out, idx, score, ridx, ralpha)
+                       K, idx, score, rmask, ralpha)
     switch (M) {
         case 16: RSM_ROUTE_LAUNCH(16); break;
         case 32: RSM_ROUTE_LAUNCH(32); break;
@@ -154,20 +144,20 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx, float* score,
                       hipStream_t stream) {
     if (dtype == RSM_F32)
-        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, 0, idx,
-                                         score, nullptr, nullptr, stream);
-    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, 0, idx, score,
+        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+                                         nullptr, nullptr, stream);
+    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
                                       nullptr, nullptr, stream);
 }
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int dense_out, int32_t* idx_out, uint8_t* ridx, float* ralpha, hipStream_t stream) {
+                     int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
     const long n_rows = B * T * Hh;
     if (dtype == RSM_F32)
-        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, dense_out,
-                                        idx_out, nullptr, ridx, ralpha, stream);
-    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, dense_out,
-                                     idx_out, nullptr, ridx, ralpha, stream);
+        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+                                        nullptr, rmask, ralpha, stream);
+    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+                                     nullptr, rmask, ralpha, stream);
 }
 
 }  // namespace rsm

@@ -99,16 +99,18 @@ def test_workspace_size(lib):
     assert f(1, 8, 0, 8, 64, 128, 64, 16) == 0
     assert f(1, 8, 2048, 8, 48, 128, 64, 16) == 0      # unsupported M
     assert f(1, 8, 2048, 8, 64, 128, 64, 65) == 0      # K > M
-    # the compact route: K slots (1 byte) and K decay factors (4 bytes) per padded token-head
-    assert f(1, 8, 2048, 8, 64, 128, 64, 16) >= 8 * 2048 * 8 * 16 * 5
-    assert f(1, 1, 100, 2, 64, 128, 64, 16) >= 1 * 128 * 2 * 16 * 5   # T padded to whole chunks
+    # the route: a 64-bit selection mask per 64 slots and K decay factors (4 bytes) per
+    # padded token-head
+    assert f(1, 8, 2048, 8, 64, 128, 64, 16) >= 8 * 2048 * 8 * (8 + 16 * 4)
+    assert f(1, 1, 100, 2, 64, 128, 64, 16) >= 1 * 128 * 2 * (8 + 16 * 4)   # T padded to whole chunks
+    assert f(1, 1, 100, 2, 128, 64, 32, 16) >= 1 * 128 * 2 * (16 + 16 * 4)  # two mask words
     assert f(1, 1, 4096, 8, 64, 128, 64, 16) > f(1, 1, 2048, 8, 64, 128, 64, 16)
     # few heads: the sequence is cut into segments whose fp32 end states (M x Dv per head
     # and segment) also live in the workspace; 8 heads of 32 chunks give 32 segments
-    assert f(1, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * 16 * 5 + 8 * 31 * 64 * 128 * 4
+    assert f(1, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * (8 + 16 * 4) + 8 * 31 * 64 * 128 * 4
     # enough heads for the whole chip: one segment, the route only
-    assert f(1, 64, 2048, 8, 64, 128, 64, 16) < 64 * 2048 * 8 * 16 * 5 + 4096
-    assert f(0, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * 16 * 5
+    assert f(1, 64, 2048, 8, 64, 128, 64, 16) < 64 * 2048 * 8 * (8 + 16 * 4) + 4096
+    assert f(0, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * (8 + 16 * 4)
 
 
 def dec(lib, dtype=1, B=4, Hh=2, M=64, Dv=128, K=8, H=F_, o=G_, idx=None, q=A):
