@@ -248,6 +248,41 @@ __device__ __forceinline__ void dma_tile(void* lds, int nbytes, int w, int lane,
 
 constexpr int pad1k(int bytes) { return (bytes + 1023) / 1024 * 1024; }
 
+// Direct loads of a row-major chunk tile of NBYTES (a multiple of 1024) whose rows are RB
+// bytes of a global row every gpitch bytes.  Wave w issues instructions r = w, w + NW, ...;
+// instruction r moves tile bytes [r*1024, r*1024 + 1024), lane l the 16 bytes at
+// r*1024 + 16*l.  The per-lane global offsets are computed once; rows at or past the
+// sequence end (only in a chunk with fewer than NBYTES / RB valid rows) repeat the last
+// valid row.
+template <int NBYTES, int RB, int NW>
+struct TileDma {
+    static constexpr int NI = (NBYTES / 1024 + NW - 1) / NW;  // instructions per wave, at most
+    static constexpr int ROWS = NBYTES / RB;                  // rows the tile spans, padding included
+    long goff[NI];
+    __device__ __forceinline__ void init(int w, int lane, long gpitch) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int off = (w + NW * j) * 1024 + 16 * lane;
+            goff[j] = long(off / RB) * gpitch + off % RB;
+        }
+    }
+    __device__ __forceinline__ void issue(void* lds, const char* base, int w, int lane, int nv, long gpitch) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int r = w + NW * j;
+            if (NBYTES % (1024 * NW) == 0 || r * 1024 < NBYTES) {
+                long go = goff[j];
+                if (nv < ROWS) {
+                    const int off = r * 1024 + 16 * lane;
+                    go = long(min(off / RB, nv - 1)) * gpitch + off % RB;
+                }
+                __builtin_amdgcn_global_load_lds(base + go, (lds_void*)(static_cast<unsigned char*>(lds) + r * 1024),
+                                                 16, 0, 0);
+            }
+        }
+    }
+};
+
 // Workgroup barrier without a memory fence.  A workgroup-scope release fence would also
 // wait for every direct global->LDS load still in flight; the scan waits for those
 // explicitly, one chunk later.  LDS is coherent inside the workgroup, so each wave's own
@@ -276,6 +311,38 @@ __device__ __forceinline__ float wave_scan_mul(float x) {
     x = scan_mul_step<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
     x = scan_mul_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+// The same scan on N independent values with the DPP folded into the multiply: a lane whose
+// source lane is outside the row (or whose row is masked off) is not written and keeps its
+// value.  A DPP read of a VGPR needs two instructions after the VALU write of that VGPR:
+// the s_nop covers the writes before the first step, and with N >= 3 values interleaved
+// every later step reads registers written N instructions earlier.
+#define RSM_SCAN_STEP(CTRL)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) asm volatile("v_mul_f32_dpp %0, %0, %0 " CTRL   \
+                                                               " bank_mask:0xf"                  \
+                                                               : "+v"(x[i]));
+template <int N>
+__device__ __forceinline__ void wave_scan_mul_n(float (&x)[N]) {
+    if constexpr (N < 3) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = wave_scan_mul(x[i]);
+    } else {
+        asm volatile("s_nop 1");
+        RSM_SCAN_STEP("row_shr:1 row_mask:0xf")
+        RSM_SCAN_STEP("row_shr:2 row_mask:0xf")
+        RSM_SCAN_STEP("row_shr:4 row_mask:0xf")
+        RSM_SCAN_STEP("row_shr:8 row_mask:0xf")
+        RSM_SCAN_STEP("row_bcast:15 row_mask:0xa")
+        RSM_SCAN_STEP("row_bcast:31 row_mask:0xc")
+    }
+}
+#undef RSM_SCAN_STEP
+
+// alpha clamped below at e^-30 for the factored path: alpha is in [0, 1], so the larger
+// value is the larger bit pattern (one integer max, no NaN canonicalisation).
+__device__ __forceinline__ float clamp_alpha(float a) {
+    return __int_as_float(max(__float_as_int(a), __float_as_int(kAlphaMin)));
 }
 
 // N consecutive input elements (N*sizeof(T) a multiple of 4 bytes, aligned) -> fp32
@@ -411,6 +478,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // wave index in a scalar register: every branch on it is a uniform scalar branch (no
     // EXEC masking around the MFMAs, which would not be skipped lane by lane)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(w >= 0 && w < NW);
     const int gT = w / NTC;
     const int Tt = (gT & 1) ? NTC - 1 - w % NTC : w % NTC;
     const int I = w % NTM, gI = w / NTM;
@@ -420,31 +488,21 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
 
     // ---- direct loads of chunk c's inputs (rows past the sequence end repeat the last row;
     // their tokens carry no route entries, so they contribute nothing)
+    const long qk_pitch = rstride * M * long(sizeof(T)), v_pitch = rstride * Dv * long(sizeof(T));
+    TileDma<int(sizeof(rk)), M * int(sizeof(T)), NW> dqk;
+    TileDma<int(sizeof(rv0)), DT * int(sizeof(T)), NW> dv;
+    dqk.init(w, lane, qk_pitch);
+    dv.init(w, lane, v_pitch);
     auto issue_qk = [&](long c) {
         const int nv = int(T_len - c * C < C ? T_len - c * C : C);
-        constexpr int RB = M * int(sizeof(T));
-        const char* kb_ = reinterpret_cast<const char*>(k + ((b * T_len + c * C) * rstride + h) * M);
-        dma_tile<NW>(rk, int(sizeof(rk)), w, lane, [&](int off) {
-            const int t = min(off / RB, nv - 1), cb = off % RB;
-            return static_cast<const void*>(kb_ + long(t) * rstride * RB + cb);
-        });
-        if (!pass_a) {
-            const char* qb = reinterpret_cast<const char*>(q + ((b * T_len + c * C) * rstride + h) * M);
-            dma_tile<NW>(rq, int(sizeof(rq)), w, lane, [&](int off) {
-                const int t = min(off / RB, nv - 1), cb = off % RB;
-                return static_cast<const void*>(qb + long(t) * rstride * RB + cb);
-            });
-        }
+        const long row0 = ((b * T_len + c * C) * rstride + h) * M;
+        dqk.issue(rk, reinterpret_cast<const char*>(k + row0), w, lane, nv, qk_pitch);
+        if (!pass_a) dqk.issue(rq, reinterpret_cast<const char*>(q + row0), w, lane, nv, qk_pitch);
     };
     auto issue_v = [&](long c, T* dst) {
         const int nv = int(T_len - c * C < C ? T_len - c * C : C);
-        const char* vb = reinterpret_cast<const char*>(v + ((b * T_len + c * C) * rstride + h) * Dv + d0);
-        constexpr int RB = DT * int(sizeof(T));
-        const long gpitch = rstride * Dv * long(sizeof(T));
-        dma_tile<NW>(dst, int(sizeof(rv0)), w, lane, [&](int off) {
-            const int t = min(off / RB, nv - 1), cb = off % RB;
-            return static_cast<const void*>(vb + t * gpitch + cb);
-        });
+        dv.issue(dst, reinterpret_cast<const char*>(v + ((b * T_len + c * C) * rstride + h) * Dv + d0), w, lane, nv,
+                 v_pitch);
     };
     auto issue_route = [&](long c) {
         const char* ab = reinterpret_cast<const char*>(ralpha + (bh * T_pad + c * C) * K);
@@ -540,8 +598,10 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         }
         int bad = 0;
 #pragma unroll
+        for (int j = 0; j < SPW; ++j) Ev[j] = clamp_alpha(al[j]);
+        wave_scan_mul_n<SPW>(Ev);
+#pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            Ev[j] = wave_scan_mul(fmaxf(al[j], kAlphaMin));
             const float el = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Ev[j]), 63));
             bad |= !(el >= kSafeMin);
         }
@@ -554,10 +614,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             float x[SPW];
             load_row<SPW>(rk, lane * M + s0, x);
 #pragma unroll
-            for (int j = 0; j < SPW; ++j) {
-                const float a = fmaxf(al[j], kAlphaMin);
-                x[j] = a < 1.0f ? x[j] * (1.0f - a) * __builtin_amdgcn_rcpf(Ev[j]) : 0.0f;
-            }
+            for (int j = 0; j < SPW; ++j) x[j] = x[j] * (1.0f - clamp_alpha(al[j])) * __builtin_amdgcn_rcpf(Ev[j]);
             P::template put_row<SPW>(sQK, psQ, oK + lane * QP + s0, x);
             if (!pass_a) {
                 load_row<SPW>(rq, lane * M + s0, x);
@@ -644,62 +701,78 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             issue_route(c + 1);
         }
 
-        // ---- S^T = Kh Qh^T (masked) and O^T = V^T P^T + H_c^T Qh^T for chunk-row tile Tt
-        if (!pass_a) {
+        // ---- S^T = Kh Qh^T (masked) and O^T = V^T P^T + H_c^T Qh^T for chunk-row tile TT
+        // (a compile-time tile index, so the masked tiles and k-blocks drop out statically)
+        auto so_phase = [&](auto ttc) __attribute__((always_inline)) {
+            constexpr int TT = decltype(ttc)::value;
             float* obase = o + ((b * T_len + tokc) * rstride + h) * Dv + d0;
             dfrag qf[NKM];
 #pragma unroll
             for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                 for (int pl = 0; pl < NPL; ++pl)
-                    qf[kb].p[pl] = P::ld(sQK, pl * psQ + (16 * Tt + l16) * QP + kb * KB + EPL * q4);
+                    qf[kb].p[pl] = P::ld(sQK, pl * psQ + (16 * TT + l16) * QP + kb * KB + EPL * q4);
             floatx4 st[NTCP];
 #pragma unroll
             for (int J = 0; J < NTCP; ++J) {
                 st[J] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (J <= Tt && J < NTC) {
-                    dfrag a[NKM];
+                if constexpr (true) {
+                    if (J <= TT && J < NTC) {
+                        dfrag a[NKM];
+#pragma unroll
+                        for (int kb = 0; kb < NKM; ++kb)
+#pragma unroll
+                            for (int pl = 0; pl < NPL; ++pl)
+                                a[kb].p[pl] = P::ld(sQK, oK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
+#pragma unroll
+                        for (int kb = 0; kb < NKM; ++kb) st[J] = P::mm_dd(a[kb], qf[kb], st[J]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * q4 + r > l16) st[TT][r] = 0.0f;  // j > t on the diagonal tile
+            dfrag pf[NKC];
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) pf[kb] = P::pack_perm(st, kb);
+            const int tl = 16 * TT + l16;
+            floatx4 acc[NOD];
+#pragma unroll
+            for (int jd = 0; jd < NOD; ++jd) {
+                const int D = gT + GT * jd;
+                acc[jd] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (NTD % GT == 0 || D < NTD) {
+                    frag va[NKC];
+                    dfrag ha[NKM];
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb)
+                        if (kb * KB < 16 * (TT + 1)) va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);
 #pragma unroll
                     for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                         for (int pl = 0; pl < NPL; ++pl)
-                            a[kb].p[pl] = P::ld(sQK, oK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
+                            ha[kb].p[pl] = P::template ld_col<false>(sH, pl * psH + 16 * D, HP, kb, q4, l16);
 #pragma unroll
-                    for (int kb = 0; kb < NKM; ++kb) st[J] = P::mm_dd(a[kb], qf[kb], st[J]);
-                    if (J == Tt) {
+                    for (int kb = 0; kb < NKC; ++kb)
+                        if (kb * KB < 16 * (TT + 1)) acc[jd] = P::mm_vd(va[kb], pf[kb], acc[jd]);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (4 * q4 + r > l16) st[J][r] = 0.0f;  // j > t
-                    }
+                    for (int kb = 0; kb < NKM; ++kb) acc[jd] = P::mm_dd(ha[kb], qf[kb], acc[jd]);
                 }
             }
-            dfrag pf[NKC];
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) pf[kb] = P::pack_perm(st, kb);
-            const int tl = 16 * Tt + l16;
 #pragma unroll
             for (int jd = 0; jd < NOD; ++jd) {
                 const int D = gT + GT * jd;
-                if (NTD % GT != 0 && D >= NTD) break;
-                frag va[NKC];
-                dfrag ha[NKM];
-#pragma unroll
-                for (int kb = 0; kb < NKC; ++kb)
-                    va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);  // in bounds for every kb
-#pragma unroll
-                for (int kb = 0; kb < NKM; ++kb)
-#pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl)
-                        ha[kb].p[pl] = P::template ld_col<false>(sH, pl * psH + 16 * D, HP, kb, q4, l16);
-                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < NKC; ++kb)
-                    if (kb * KB < 16 * (Tt + 1)) acc = P::mm_vd(va[kb], pf[kb], acc);
-#pragma unroll
-                for (int kb = 0; kb < NKM; ++kb) acc = P::mm_dd(ha[kb], qf[kb], acc);
-                if (tl < nvalid)
+                if ((NTD % GT == 0 || D < NTD) && tl < nvalid)
                     *reinterpret_cast<float4*>(obase + tl * rstride * Dv + 16 * D + 4 * q4) =
-                        make_float4(acc[0], acc[1], acc[2], acc[3]);
+                        make_float4(acc[jd][0], acc[jd][1], acc[jd][2], acc[jd][3]);
+            }
+        };
+        if (!pass_a) {
+            switch (Tt) {
+                case 0: so_phase(std::integral_constant<int, 0>{}); break;
+                case 1: if constexpr (NTC > 1) so_phase(std::integral_constant<int, 1>{}); break;
+                case 2: if constexpr (NTC > 2) so_phase(std::integral_constant<int, 2>{}); break;
+                case 3: if constexpr (NTC > 3) so_phase(std::integral_constant<int, 3>{}); break;
             }
         }
 
