@@ -67,9 +67,38 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // a+12; so lane (a + 4e) addresses row rho(e), columns 4a..4a+3.
 // ------------------------------------------------------------------------------------
 //
+// Swizzled tiles.  The raw q, k and v tiles arrive in LDS by direct loads that fill 16-byte
+// granules in order, so their rows cannot be padded; instead granule g of row `row` (GPR
+// granules per row) sits at granule position row*GPR + swz(row, g), an XOR of g with a
+// function of the row, so that the rows a wave reads at once fall into different banks:
+//  * KIND 1 (q, k: lane = row, one granule each): g ^ ((row / RPB) % GPR);
+//  * KIND 2 (v: 8-byte column pieces of 4 rows and 2 adjacent granules per 16 lanes):
+//    g ^ 2*((row / RPB) % (GPR/2)), which keeps granule pairs together;
+//  * KIND 3 (the state copy: 8-byte column pieces of rows 8*q4 + 0..3 per 16 lanes):
+//    g ^ ((2*(row % 4) + 8*((row / 8) % 2)) % GPR);
+// with RPB = max(1, 16 / GPR) rows per 256-byte bank sweep.
+//
 // Every LDS access is written as one offset from its array (arr + off): the compiler then
 // keeps track of which array each access touches and does not make it wait for the direct
 // global->LDS loads still in flight into other arrays.
+template <int GPR, int KIND>
+__device__ __forceinline__ int swz(int row, int g) {
+    if constexpr (GPR <= 1 || KIND == 0) {
+        return g;
+    } else {
+        constexpr int RPB = GPR >= 16 ? 1 : 16 / GPR;
+        if constexpr (KIND == 1) return g ^ ((row / RPB) % GPR);
+        else if constexpr (KIND == 3) return g ^ ((2 * (row & 3) + 8 * ((row >> 3) & 1)) & (GPR - 1));
+        else if constexpr (GPR >= 4) return g ^ (2 * ((row / RPB) % (GPR / 2)));
+        else return g;
+    }
+}
+// element index of (row, col) in a swizzled tile of EPG elements per granule
+template <int GPR, int KIND, int EPG>
+__device__ __forceinline__ int swz_elem(int row, int col) {
+    return (row * GPR + swz<GPR, KIND>(row, col / EPG)) * EPG + col % EPG;
+}
+
 template <typename T> struct Pol;
 
 template <> struct Pol<float> {
@@ -88,6 +117,11 @@ template <> struct Pol<float> {
     __device__ static __forceinline__ frag ld_col(const E* arr, int off0, int pitch, int kb, int q4, int l16) {
         const int row = PERM ? jperm(kb, q4, 0) : inat(kb, q4, 0);
         return arr[off0 + row * pitch + l16];
+    }
+    template <bool PERM, int GPR, int KIND>
+    __device__ static __forceinline__ frag ld_col_swz(const E* arr, int base, int col0, int kb, int q4, int l16) {
+        const int row = PERM ? jperm(kb, q4, 0) : inat(kb, q4, 0);
+        return arr[base + swz_elem<GPR, KIND, 4>(row, col0 + l16)];
     }
     __device__ static __forceinline__ void put(E* arr, int ps, int i, float x) { arr[i] = x; }
     // 4 consecutive values (16-byte aligned)
@@ -140,6 +174,18 @@ template <> struct Pol<bf16_t> {
         const int r1 = PERM ? jperm(kb, q4, 4 + er) : inat(kb, q4, 4 + er);
         const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (off0 + r0 * pitch + c4)));
         const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (off0 + r1 * pitch + c4)));
+        const uint2 xa = __builtin_bit_cast(uint2, x), ya = __builtin_bit_cast(uint2, y);
+        return __builtin_bit_cast(frag, make_uint4(xa.x, xa.y, ya.x, ya.y));
+    }
+    template <bool PERM, int GPR, int KIND>
+    __device__ static __forceinline__ frag ld_col_swz(const E* arr, int base, int col0, int kb, int q4, int l16) {
+        const int er = l16 >> 2, c = col0 + 4 * (l16 & 3);
+        const int r0 = PERM ? jperm(kb, q4, er) : inat(kb, q4, er);
+        const int r1 = PERM ? jperm(kb, q4, 4 + er) : inat(kb, q4, 4 + er);
+        const shortx4 x =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (base + swz_elem<GPR, KIND, 8>(r0, c))));
+        const shortx4 y =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(arr + (base + swz_elem<GPR, KIND, 8>(r1, c))));
         const uint2 xa = __builtin_bit_cast(uint2, x), ya = __builtin_bit_cast(uint2, y);
         return __builtin_bit_cast(frag, make_uint4(xa.x, xa.y, ya.x, ya.y));
     }
@@ -248,34 +294,33 @@ __device__ __forceinline__ void dma_tile(void* lds, int nbytes, int w, int lane,
 
 constexpr int pad1k(int bytes) { return (bytes + 1023) / 1024 * 1024; }
 
-// Direct loads of a row-major chunk tile of NBYTES (a multiple of 1024) whose rows are RB
+// Direct loads of a swizzled chunk tile of NBYTES (a multiple of 1024) whose rows are RB
 // bytes of a global row every gpitch bytes.  Wave w issues instructions r = w, w + NW, ...;
-// instruction r moves tile bytes [r*1024, r*1024 + 1024), lane l the 16 bytes at
-// r*1024 + 16*l.  The per-lane global offsets are computed once; rows at or past the
-// sequence end (only in a chunk with fewer than NBYTES / RB valid rows) repeat the last
-// valid row.
-template <int NBYTES, int RB, int NW>
+// instruction r fills tile granules 64r .. 64r + 63, lane l granule p = 64r + l, which holds
+// granule swz(row, p % GPR) of row p / GPR (the swizzle is an XOR, its own inverse).  The
+// per-lane global offsets are computed once; rows at or past the sequence end (only in a
+// chunk with fewer than NBYTES / RB valid rows) repeat the last valid row.
+template <int NBYTES, int RB, int NW, int KIND>
 struct TileDma {
     static constexpr int NI = (NBYTES / 1024 + NW - 1) / NW;  // instructions per wave, at most
     static constexpr int ROWS = NBYTES / RB;                  // rows the tile spans, padding included
+    static constexpr int GPR = RB / 16;
     long goff[NI];
+    __device__ static __forceinline__ long offset(int p, int nrow_max, long gpitch) {
+        const int row = p / GPR;
+        const int g = swz<GPR, KIND>(row, p % GPR);
+        return long(min(row, nrow_max)) * gpitch + 16 * g;
+    }
     __device__ __forceinline__ void init(int w, int lane, long gpitch) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            const int off = (w + NW * j) * 1024 + 16 * lane;
-            goff[j] = long(off / RB) * gpitch + off % RB;
-        }
+        for (int j = 0; j < NI; ++j) goff[j] = offset((w + NW * j) * 64 + lane, ROWS, gpitch);
     }
     __device__ __forceinline__ void issue(void* lds, const char* base, int w, int lane, int nv, long gpitch) const {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int r = w + NW * j;
             if (NBYTES % (1024 * NW) == 0 || r * 1024 < NBYTES) {
-                long go = goff[j];
-                if (nv < ROWS) {
-                    const int off = r * 1024 + 16 * lane;
-                    go = long(min(off / RB, nv - 1)) * gpitch + off % RB;
-                }
+                const long go = nv < ROWS ? offset(r * 64 + lane, nv - 1, gpitch) : goff[j];
                 __builtin_amdgcn_global_load_lds(base + go, (lds_void*)(static_cast<unsigned char*>(lds) + r * 1024),
                                                  16, 0, 0);
             }
@@ -385,6 +430,22 @@ __device__ __forceinline__ void load_row(const float* arr, int off, float (&x)[N
     }
 }
 
+// N consecutive elements of row `row` from column col0 of a swizzled tile (col0 a multiple
+// of min(N, elements per granule)); read granule piece by granule piece
+template <int N, int GPR, int KIND, typename T>
+__device__ __forceinline__ void load_row_swz(const T* arr, int row, int col0, float (&x)[N]) {
+    constexpr int EPG = 16 / int(sizeof(T));
+    constexpr int PE = N < EPG ? N : EPG;  // elements per piece
+#pragma unroll
+    for (int pc = 0; pc < N / PE; ++pc) {
+        float y[PE];
+        load_row<PE>(arr, swz_elem<GPR, KIND, EPG>(row, col0 + pc * PE), y);
+#pragma unroll
+        for (int e = 0; e < PE; ++e) x[pc * PE + e] = y[e];
+    }
+}
+
+
 // ------------------------------------------------------------------------------------
 // Sequence segments.  A head's chunks are cut into S consecutive segments so that a launch
 // has enough workgroups.  Segment s starts from the state the segments before it leave:
@@ -428,7 +489,10 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int CP = C > KB ? C : KB;        // padded chunk dimension (k of row contractions)
     constexpr int EVE = 16 / int(sizeof(E));   // elements per 16 bytes
     constexpr int QP = MP + EVE;               // pitch of Qh / Kh rows
-    constexpr int HP = DT + EVE;               // pitch of state rows
+    constexpr int GH = DT * int(sizeof(E)) / 16;   // granules per row of the state copy (swizzled)
+    constexpr int GQK = M * int(sizeof(T)) / 16;   // granules per row of the q / k tiles
+    constexpr int GV = DT * int(sizeof(T)) / 16;   // granules per row of the v tile
+    constexpr int EPG = 16 / int(sizeof(T));       // elements per granule
     constexpr int NTC = C / 16, NTCP = CP / 16, NTD = DT / 16, NTM = M / 16;
     constexpr int NKM = MP / KB, NKC = CP / KB;
     constexpr int GT = NW / NTC;               // waves per chunk-row tile
@@ -439,7 +503,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int MW = (M + 63) / 64;          // 64-bit words of a token's selection mask
     constexpr int psQ = CP * QP + 8;           // plane stride of Qh / Kh
     constexpr int oK = NPL * psQ;              // Kh planes start here
-    constexpr int psH = MP * HP;               // plane stride of the state copy
+    constexpr int psH = MP * DT;               // plane stride of the state copy
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int SZHF = M * DT * 4 / int(sizeof(E));
     static_assert(NW % NTC == 0 && NW % NTM == 0 && SPW >= 2 && SPW <= 16 && C <= 64, "tile split");
@@ -489,8 +553,8 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // ---- direct loads of chunk c's inputs (rows past the sequence end repeat the last row;
     // their tokens carry no route entries, so they contribute nothing)
     const long qk_pitch = rstride * M * long(sizeof(T)), v_pitch = rstride * Dv * long(sizeof(T));
-    TileDma<int(sizeof(rk)), M * int(sizeof(T)), NW> dqk;
-    TileDma<int(sizeof(rv0)), DT * int(sizeof(T)), NW> dv;
+    TileDma<int(sizeof(rk)), M * int(sizeof(T)), NW, 1> dqk;
+    TileDma<int(sizeof(rv0)), DT * int(sizeof(T)), NW, 2> dv;
     dqk.init(w, lane, qk_pitch);
     dv.init(w, lane, v_pitch);
     auto issue_qk = [&](long c) {
@@ -545,7 +609,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
             const int D = gI + GI * j, i = 16 * I + l16;
-            if (D < NTD) P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+            if (D < NTD) P::put4(sH, psH, swz_elem<GH, 3, EVE>(i, 16 * D + 4 * q4), Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
         }
     }
     if (c_begin < c_end) {
@@ -591,7 +655,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
                 const bool sel = (g >> j) & 1u;
-                const float a = rA[tc * K + (idx < K ? idx : K - 1)];
+                const float a = rA[(idx < K ? idx : K - 1) * C + tc];
                 al[j] = sel ? a : 1.0f;
                 idx += sel ? 1 : 0;
             }
@@ -612,12 +676,12 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         if (lane == 0) sFlag[w] = bad;
         if (lane < C) {
             float x[SPW];
-            load_row<SPW>(rk, lane * M + s0, x);
+            load_row_swz<SPW, GQK, 1>(rk, lane, s0, x);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) x[j] = x[j] * (1.0f - clamp_alpha(al[j])) * __builtin_amdgcn_rcpf(Ev[j]);
             P::template put_row<SPW>(sQK, psQ, oK + lane * QP + s0, x);
             if (!pass_a) {
-                load_row<SPW>(rq, lane * M + s0, x);
+                load_row_swz<SPW, GQK, 1>(rq, lane, s0, x);
 #pragma unroll
                 for (int j = 0; j < SPW; ++j) x[j] *= Ev[j];
                 P::template put_row<SPW>(sQK, psQ, lane * QP + s0, x);
@@ -651,14 +715,15 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                     const int i = e / DT, dd = e % DT;
                     const float a = rA[tt * M + i];
                     if (a != 1.0f) {
-                        const float wk = (1.0f - a) * Elem<T>::load(rk, tt * M + i);
-                        sHf[e] = fmaf(a, sHf[e], wk * Elem<T>::load(rvc, tt * DT + dd));
+                        const float wk = (1.0f - a) * Elem<T>::load(rk, swz_elem<GQK, 1, EPG>(tt, i));
+                        sHf[e] = fmaf(a, sHf[e], wk * Elem<T>::load(rvc, swz_elem<GV, 2, EPG>(tt, dd)));
                     }
                 }
                 wg_barrier();
                 if (!pass_a && tid < DT) {
                     float acc = 0.0f;
-                    for (int i = 0; i < M; ++i) acc = fmaf(Elem<T>::load(rq, tt * M + i), sHf[i * DT + tid], acc);
+                    for (int i = 0; i < M; ++i)
+                        acc = fmaf(Elem<T>::load(rq, swz_elem<GQK, 1, EPG>(tt, i)), sHf[i * DT + tid], acc);
                     o[((b * T_len + tokc + tt) * rstride + h) * Dv + d0 + tid] = acc;
                 }
                 wg_barrier();
@@ -684,7 +749,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                 for (int j = 0; j < UPW; ++j) {
                     const int D = gI + GI * j, i = 16 * I + l16;
                     if (D < NTD)
-                        P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+                        P::put4(sH, psH, swz_elem<GH, 3, EVE>(i, 16 * D + 4 * q4), Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
                 }
             } else {
                 Eseg *= sE[16 * I + l16];
@@ -746,12 +811,12 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                     dfrag ha[NKM];
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
-                        if (kb * KB < 16 * (TT + 1)) va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);
+                        if (kb * KB < 16 * (TT + 1)) va[kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * D, kb, q4, l16);
 #pragma unroll
                     for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
                         for (int pl = 0; pl < NPL; ++pl)
-                            ha[kb].p[pl] = P::template ld_col<false>(sH, pl * psH + 16 * D, HP, kb, q4, l16);
+                            ha[kb].p[pl] = P::template ld_col_swz<false, GH, 3>(sH, pl * psH, 16 * D, kb, q4, l16);
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
                         if (kb * KB < 16 * (TT + 1)) acc[jd] = P::mm_vd(va[kb], pf[kb], acc[jd]);
@@ -792,7 +857,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                 if (D < NTD) {
                     frag va[NKC];
 #pragma unroll
-                    for (int kb = 0; kb < NKC; ++kb) va[kb] = P::template ld_col<true>(rvc, 16 * D, DT, kb, q4, l16);
+                    for (int kb = 0; kb < NKC; ++kb) va[kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * D, kb, q4, l16);
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb) U[j] = P::mm_vd(va[kb], kf[kb], U[j]);
                 }
@@ -807,7 +872,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Hreg[j][r] = e * (Hreg[j][r] + U[j][r]);
                 if (!pass_a)
-                    P::put4(sH, psH, i * HP + 16 * D + 4 * q4, Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
+                    P::put4(sH, psH, swz_elem<GH, 3, EVE>(i, 16 * D + 4 * q4), Hreg[j][0], Hreg[j][1], Hreg[j][2], Hreg[j][3]);
             }
         }
         if (pass_a) Eseg *= e;
@@ -981,7 +1046,8 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
     auto* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
     const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),
                      reinterpret_cast<float*>(ws + L.de_off)};
-    int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, idx_out, rmask, ralpha, stream);
+    int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.chunk, idx_out, rmask, ralpha,
+                              stream);
     if (st != RSM_OK) return st;
     const ScanArgs a{q, k, v, H0, B, T, Hh, Dv, K, sg, rmask, ralpha, o, H_out, stream};
     if (dtype == RSM_F32) return dispatch_m<float>(M, L.chunk, L.dt, a);

@@ -19,8 +19,8 @@ int decode_step_launch(const void* q, const void* k, const void* z, const void* 
 
 // Workspace of the chunked forward: the route of every token-head in (batch*head, padded
 // token) order -- a selection bit mask (uint64 words) and the alphas of the selected slots
-// (fp32, ascending slot order) -- then the state and decay product of every sequence
-// segment but the last; byte offsets and total.
+// (fp32, ascending slot order, slot-major within each chunk) -- then the state and decay
+// product of every sequence segment but the last; byte offsets and total.
 struct FwdLayout {
     size_t rmask_off, ralpha_off;  // route
     size_t dh_off, de_off;         // per-segment states and decay products (S > 1)
@@ -34,7 +34,7 @@ struct FwdLayout {
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream);
+                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream);
 
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,

@@ -52,13 +52,15 @@ template <int M> struct RowRegs<float, M> {
 };
 
 // kFwd = false: public router (idx int32 [row][K], score [row][K] or NULL).
-// kFwd = true : forward router, rows written in (b*Hh + h, t) order with T_pad tokens per
-//               head: rmask uint64 [..][MW] (bit i%64 of word i/64 set iff slot i is
-//               selected, MW = ceil(M/64)) and ralpha fp32 [..][K] in ascending slot order;
-//               idx int32 [row][K] or NULL.
+// kFwd = true : forward router, rows in (b*Hh + h, t) order with T_pad tokens per head
+//               (T_pad a multiple of the chunk length C): rmask uint64 [..][MW] (bit i%64 of
+//               word i/64 set iff slot i is selected, MW = ceil(M/64)), and the alphas of the
+//               selected slots in ascending slot order, stored per chunk as [n][C] (entry n
+//               of token t of the chunk at n*C + t%C) so that the tokens of a chunk read one
+//               entry each from consecutive words; idx int32 [row][K] or NULL.
 template <typename T, int M, bool kFwd>
 __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z, const float* __restrict__ f,
-                                                        long n_rows, long T_len, int Hh, long T_pad, int K,
+                                                        long n_rows, long T_len, int Hh, long T_pad, int K, int C,
                                                         int32_t* __restrict__ idx, float* __restrict__ score,
                                                         unsigned long long* __restrict__ rmask,
                                                         float* __restrict__ ralpha) {
@@ -83,6 +85,7 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
         constexpr int MW = (M + 63) / 64;
         const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
         const long orow = (b * Hh + h) * T_pad + t;
+        float* alist = ralpha + ((b * Hh + h) * T_pad + (t - t % C)) * K + t % C;  // entry n at alist[n*C]
         const float ft = f[row];
         unsigned long long mk[MW];
 #pragma unroll
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
             if (all || RowKey<T>::make(v[i], i) >= th) {
                 mk[i >> 6] |= 1ull << (i & 63);
                 const float s = sigmoidf_dev(v[i]);
-                ralpha[orow * K + n] = s > 0.0f ? __expf(s * ft) : 1.0f;
+                alist[long(n) * C] = s > 0.0f ? __expf(s * ft) : 1.0f;
                 if (idx) idx[dst + n] = i;
                 ++n;
             }
@@ -122,14 +125,14 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 }
 
 template <typename T, bool kFwd>
-static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K,
+static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K, int C,
                        int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
     const dim3 grid(unsigned((n_rows + 63) / 64)), block(64);
     const size_t lds = (kFwd || K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane slot lists (public router)
 #define RSM_ROUTE_LAUNCH(MM)                                                                                    \
     hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, T_pad, \
-                       K, idx, score, rmask, ralpha)
+                       K, C, idx, score, rmask, ralpha)
     switch (M) {
         case 16: RSM_ROUTE_LAUNCH(16); break;
         case 32: RSM_ROUTE_LAUNCH(32); break;
@@ -144,19 +147,19 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx, float* score,
                       hipStream_t stream) {
     if (dtype == RSM_F32)
-        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+        return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, 1, idx, score,
                                          nullptr, nullptr, stream);
-    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, idx, score,
+    return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, 1, idx, score,
                                       nullptr, nullptr, stream);
 }
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
+                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
     const long n_rows = B * T * Hh;
     if (dtype == RSM_F32)
-        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+        return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, C, idx_out,
                                         nullptr, rmask, ralpha, stream);
-    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, idx_out,
+    return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, C, idx_out,
                                      nullptr, rmask, ralpha, stream);
 }
 
