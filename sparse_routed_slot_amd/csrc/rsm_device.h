@@ -151,6 +151,68 @@ __device__ __forceinline__ void bitonic_sort_desc(U (&kv)[N]) {
             }
 }
 
+// Descending bitonic merge of a bitonic sequence of 16 keys at kv[o .. o+15].
+template <typename U, int N>
+__device__ __forceinline__ void bitonic_merge_desc16(U (&kv)[N], const int o) {
+#pragma unroll
+    for (int j = 8; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int l = i ^ j;
+            if (l > i) {
+                const U a = kv[o + i], b = kv[o + l];
+                kv[o + i] = a > b ? a : b;
+                kv[o + l] = a > b ? b : a;
+            }
+        }
+}
+
+// Threshold packed key of a row for K <= 16: the K-th largest of its M distinct packed keys.
+// Each group of 16 keys is sorted descending by a bitonic network; groups are then merged
+// pairwise keeping only the top 16 (the elementwise maximum of one sorted list and the other
+// reversed holds the top 16 of the union as a bitonic sequence, which a bitonic merge sorts).
+template <typename T, int M>
+__device__ __forceinline__ typename RowKey<T>::type row_threshold16(const float (&x)[M], int K) {
+    typedef typename RowKey<T>::type U;
+    static_assert(M % 16 == 0, "groups of 16");
+    U kv[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) kv[i] = RowKey<T>::make(x[i], i);
+#pragma unroll
+    for (int g = 0; g < M; g += 16) {
+#pragma unroll
+        for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int l = i ^ j;
+                    if (l > i) {
+                        const U a = kv[g + i], b = kv[g + l];
+                        const U hi = a > b ? a : b, lo = a > b ? b : a;
+                        const bool desc = k == 16 || (i & k) == 0;
+                        kv[g + i] = desc ? hi : lo;
+                        kv[g + l] = desc ? lo : hi;
+                    }
+                }
+    }
+#pragma unroll
+    for (int span = 16; span < M; span <<= 1)
+#pragma unroll
+        for (int g = 0; g < M; g += 2 * span) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const U a = kv[g + i], b = kv[g + span + 15 - i];
+                kv[g + i] = a > b ? a : b;
+            }
+            bitonic_merge_desc16<U, M>(kv, g);
+        }
+    U th = kv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) th = (r == K - 1) ? kv[r] : th;
+    return th;
+}
+
 // Threshold packed key of a row: the K-th largest of its M packed keys (K uniform).
 template <typename T, int M>
 __device__ __forceinline__ typename RowKey<T>::type row_threshold(const float (&x)[M], int K) {

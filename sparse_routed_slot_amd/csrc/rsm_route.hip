@@ -58,7 +58,8 @@ template <int M> struct RowRegs<float, M> {
 //               selected slots in ascending slot order, stored per chunk as [n][C] (entry n
 //               of token t of the chunk at n*C + t%C) so that the tokens of a chunk read one
 //               entry each from consecutive words; idx int32 [row][K] or NULL.
-template <typename T, int M, bool kFwd>
+// SMALLK: K <= 16, threshold by the partial top-16 network; otherwise a full sort.
+template <typename T, int M, bool kFwd, bool SMALLK>
 __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z, const float* __restrict__ f,
                                                         long n_rows, long T_len, int Hh, long T_pad, int K, int C,
                                                         int32_t* __restrict__ idx, float* __restrict__ score,
@@ -69,52 +70,67 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
     int* s_slot = reinterpret_cast<int*>(smem);              // [K][64]
     float* s_val = reinterpret_cast<float*>(smem) + K * 64;  // [K][64]
     const int lane = threadIdx.x;
-    const long row = long(blockIdx.x) * 64 + lane;
-    if (row >= n_rows) return;  // no cross-lane operations below
+    // public router: lane = row.  Forward router: a workgroup takes 64 consecutive tokens of
+    // one (b, h), so the route it writes (per token, and per chunk slot-major) is contiguous.
+    long row, t = 0, bh = 0;
+    if (kFwd) {
+        const long nbt = (T_len + 63) / 64;
+        bh = long(blockIdx.x) / nbt;
+        t = (long(blockIdx.x) % nbt) * 64 + lane;
+        if (t >= T_len) return;  // no cross-lane operations below
+        row = ((bh / Hh) * T_len + t) * Hh + bh % Hh;
+    } else {
+        row = long(blockIdx.x) * 64 + lane;
+        if (row >= n_rows) return;
+    }
 
     RowRegs<T, M> x;
     x.load(z + row * M);
     const bool all = (K == M);
-    float v[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) v[i] = x.val(i);
     U th = 0;
-    if (!all) th = row_threshold<T, M>(v, K);
-    const long dst = row * K;
-    if (kFwd) {
-        constexpr int MW = (M + 63) / 64;
-        const long h = row % Hh, bt = row / Hh, t = bt % T_len, b = bt / T_len;
-        const long orow = (b * Hh + h) * T_pad + t;
-        float* alist = ralpha + ((b * Hh + h) * T_pad + (t - t % C)) * K + t % C;  // entry n at alist[n*C]
-        const float ft = f[row];
-        unsigned long long mk[MW];
+    if (!all) {
+        float v[M];
 #pragma unroll
-        for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < M; ++i) {
-            if (all || RowKey<T>::make(v[i], i) >= th) {
-                mk[i >> 6] |= 1ull << (i & 63);
-                const float s = sigmoidf_dev(v[i]);
-                alist[long(n) * C] = s > 0.0f ? __expf(s * ft) : 1.0f;
-                if (idx) idx[dst + n] = i;
-                ++n;
-            }
-        }
-#pragma unroll
-        for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
-        return;
+        for (int i = 0; i < M; ++i) v[i] = x.val(i);
+        if constexpr (SMALLK) th = row_threshold16<T, M>(v, K);
+        else th = row_threshold<T, M>(v, K);
     }
+
+    // selected slots in ascending order: bit mask and per-lane LDS list
+    constexpr int MW = (M + 63) / 64;
+    unsigned long long mk[MW];
+#pragma unroll
+    for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
     if (!all) {
         int n = 0;
 #pragma unroll
         for (int i = 0; i < M; ++i) {
-            if (RowKey<T>::make(v[i], i) >= th) {
+            const float vi = x.val(i);
+            if (RowKey<T>::make(vi, i) >= th) {
+                mk[i >> 6] |= 1ull << (i & 63);
                 s_slot[n * 64 + lane] = i;
-                s_val[n * 64 + lane] = v[i];
+                s_val[n * 64 + lane] = vi;
                 ++n;
             }
         }
+    } else {
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) mk[wd] = (M - 64 * wd >= 64) ? ~0ull : ((1ull << (M - 64 * wd)) - 1ull);
+    }
+    const long dst = row * K;
+    if (kFwd) {
+        const long orow = bh * T_pad + t;
+        float* alist = ralpha + (bh * T_pad + (t - t % C)) * K + t % C;  // entry n at alist[n*C]
+        const float ft = f[row];
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
+        for (int n = 0; n < K; ++n) {
+            const int i = all ? n : s_slot[n * 64 + lane];
+            const float s = sigmoidf_dev(all ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane]);
+            alist[long(n) * C] = s > 0.0f ? __expf(s * ft) : 1.0f;
+            if (idx) idx[dst + n] = i;
+        }
+        return;
     }
     for (int n = 0; n < K; ++n) {
         const int i = all ? n : s_slot[n * 64 + lane];
@@ -128,11 +144,16 @@ template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K, int C,
                        int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
-    const dim3 grid(unsigned((n_rows + 63) / 64)), block(64);
-    const size_t lds = (kFwd || K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane slot lists (public router)
-#define RSM_ROUTE_LAUNCH(MM)                                                                                    \
-    hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, T_pad, \
-                       K, C, idx, score, rmask, ralpha)
+    const long nblk = kFwd ? (n_rows / T_len) * ((T_len + 63) / 64) : (n_rows + 63) / 64;
+    const dim3 grid(static_cast<unsigned>(nblk)), block(64);
+    const size_t lds = (K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane slot lists
+#define RSM_ROUTE_LAUNCH(MM)                                                                                   \
+    if (K <= 16 && MM >= 16)                                                                                      \
+        hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, \
+                           T_pad, K, C, idx, score, rmask, ralpha);                                               \
+    else                                                                                                          \
+        hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd, false>), grid, block, lds, stream, z, f, n_rows, T_len, \
+                           Hh, T_pad, K, C, idx, score, rmask, ralpha)
     switch (M) {
         case 16: RSM_ROUTE_LAUNCH(16); break;
         case 32: RSM_ROUTE_LAUNCH(32); break;
