@@ -3,10 +3,10 @@
 // RSM router of Raven (README page, "How Raven Works": TopK(sigmoid(r_proj(x))) and
 // decay = exp(route_scores * f)), taking the projected logits z as input.
 //
-// One lane owns one row (M logits in registers); rows are contiguous in memory, so the
-// wave reads 64 consecutive rows.  The exact top-K with ties to the lower slot index comes
-// from a bitonic sort of distinct packed keys (rsm_device.h).  Selected slots are
-// collected in ascending slot order through per-lane LDS lists, then scored:
+// One lane owns one row (M logits in registers).  The exact top-K with ties to the lower
+// slot index compares distinct packed keys (order-preserving bits of z, then the inverted
+// slot index) with the K-th largest key, found by a bitonic network (rsm_device.h).  The
+// selected slots form a bit mask, walked in ascending slot order to score them:
 //  * public router: idx (int32) and score = sigmoid(z) per selected slot;
 //  * forward router: the per-token route the chunked forward consumes -- a selection bit
 //    mask over the M slots and alpha = exp(s*f) of the selected slots in ascending slot
@@ -66,9 +66,6 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
                                                         unsigned long long* __restrict__ rmask,
                                                         float* __restrict__ ralpha) {
     typedef typename RowKey<T>::type U;
-    extern __shared__ __align__(16) unsigned char smem[];
-    int* s_slot = reinterpret_cast<int*>(smem);              // [K][64]
-    float* s_val = reinterpret_cast<float*>(smem) + K * 64;  // [K][64]
     const int lane = threadIdx.x;
     // public router: lane = row.  Forward router: a workgroup takes 64 consecutive tokens of
     // one (b, h), so the route it writes (per token, and per chunk slot-major) is contiguous.
@@ -96,47 +93,48 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
         else th = row_threshold<T, M>(v, K);
     }
 
-    // selected slots in ascending order: bit mask and per-lane LDS list
+    // selected slots as a bit mask (bit i%64 of word i/64)
     constexpr int MW = (M + 63) / 64;
     unsigned long long mk[MW];
 #pragma unroll
     for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
     if (!all) {
-        int n = 0;
 #pragma unroll
-        for (int i = 0; i < M; ++i) {
-            const float vi = x.val(i);
-            if (RowKey<T>::make(vi, i) >= th) {
-                mk[i >> 6] |= 1ull << (i & 63);
-                s_slot[n * 64 + lane] = i;
-                s_val[n * 64 + lane] = vi;
-                ++n;
-            }
-        }
+        for (int i = 0; i < M; ++i)
+            if (RowKey<T>::make(x.val(i), i) >= th) mk[i >> 6] |= 1ull << (i & 63);
     } else {
 #pragma unroll
         for (int wd = 0; wd < MW; ++wd) mk[wd] = (M - 64 * wd >= 64) ? ~0ull : ((1ull << (M - 64 * wd)) - 1ull);
     }
     const long dst = row * K;
+    const T* zrow = z + row * M;
     if (kFwd) {
         const long orow = bh * T_pad + t;
-        float* alist = ralpha + (bh * T_pad + (t - t % C)) * K + t % C;  // entry n at alist[n*C]
-        const float ft = f[row];
 #pragma unroll
         for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
-        for (int n = 0; n < K; ++n) {
-            const int i = all ? n : s_slot[n * 64 + lane];
-            const float s = sigmoidf_dev(all ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane]);
+    }
+    float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
+    const float ft = kFwd ? f[row] : 0.0f;
+    // walk the selected slots in ascending order (lowest set bit first); the logit of a
+    // selected slot is read again from the row just loaded (cached)
+    unsigned long long m0 = mk[0], m1 = MW > 1 ? mk[MW - 1] : 0ull;
+    for (int n = 0; n < K; ++n) {
+        int i;
+        if (MW == 1 || m0 != 0ull) {
+            i = __builtin_ctzll(m0);
+            m0 &= m0 - 1ull;
+        } else {
+            i = 64 + __builtin_ctzll(m1);
+            m1 &= m1 - 1ull;
+        }
+        const float s = sigmoidf_dev(Elem<T>::load(zrow, i));
+        if (kFwd) {
             alist[long(n) * C] = s > 0.0f ? __expf(s * ft) : 1.0f;
             if (idx) idx[dst + n] = i;
+        } else {
+            idx[dst + n] = i;
+            if (score) score[dst + n] = s;
         }
-        return;
-    }
-    for (int n = 0; n < K; ++n) {
-        const int i = all ? n : s_slot[n * 64 + lane];
-        const float zi = all ? Elem<T>::load(z + row * M, i) : s_val[n * 64 + lane];
-        idx[dst + n] = i;
-        if (score) score[dst + n] = sigmoidf_dev(zi);
     }
 }
 
@@ -146,7 +144,7 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
     if (n_rows == 0) return RSM_OK;
     const long nblk = kFwd ? (n_rows / T_len) * ((T_len + 63) / 64) : (n_rows + 63) / 64;
     const dim3 grid(static_cast<unsigned>(nblk)), block(64);
-    const size_t lds = (K == M) ? 0 : size_t(K) * 64 * 8;  // per-lane slot lists
+    const size_t lds = 0;
 #define RSM_ROUTE_LAUNCH(MM)                                                                                   \
     if (K <= 16 && MM >= 16)                                                                                      \
         hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, \
