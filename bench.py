@@ -1,7 +1,7 @@
 """Benchmark of the RSM mixer hot path on one MI355X.
 
-A step is one rsm_forward_chunked call (route, sparse decay, chunk contractions, state
-scan, emit) over one batch of the 400M-scale layer workload: B=8, T=2048, Hh=8, M=64,
+A step is one rsm_forward_chunked call (route; then, per sequence segment, sparse decay,
+chunk contractions, state scan and emit) over one batch of the 400M-scale layer workload: B=8, T=2048, Hh=8, M=64,
 Dv=128, top-16, C=64, bf16 q/k/z/v, fp32 f/state/outputs.  Three input sets are rotated
 so the ~154 MB working set cannot sit in the 256 MB last-level cache between steps.
 The decode step (256 sequences x 16 heads, M64 Dv128 K16, prefill T=512) is timed in the
@@ -213,8 +213,8 @@ def main():
                           "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": len(pool)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel "
-                               "(two launches back to back on the caller's stream)",
+                     "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel pass A + "
+                               "fwd_scan_kernel pass B (three launches back to back on the caller's stream)",
                      "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,

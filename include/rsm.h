@@ -77,9 +77,10 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
 
 /*
  * Bytes of device workspace rsm_forward_chunked needs for these sizes (0 if T == 0).
- * The workspace holds the route of every token-head, padded to whole chunks: the K
- * selected slots (uint8) and their decay factors (fp32), 5*K bytes per token-head, or,
- * when K > min(32, M/2), the decay factor of every slot (1 outside the top K), 4*M bytes.
+ * The workspace holds the route of every token-head, padded to whole chunks (a selection
+ * bit mask, 8 bytes per 64 slots, and the K decay factors of the selected slots, fp32),
+ * and, when few heads make the forward cut each sequence into S segments, the fp32 end
+ * state (M x Dv) and decay product (M) of every segment but the last, per head.
  * Returns 0 for unsupported arguments as well; the forward call then reports the error.
  */
 size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
@@ -99,9 +100,9 @@ size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, 
  *            rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C, K) bytes (owned by the
  *            caller, contents undefined on entry and on return)
  * Slots never selected in the sequence come back in H_out bit-identical to H0.
- * C only sets how the work is cut: results agree across C up to rounding.  With fp32
- * inputs and M = 128 the kernels run C = 64 as chunks of 32 (their tiles would not fit in
- * the 160 KB of LDS of a compute unit).
+ * C only sets how the work is cut: results agree across C up to rounding.  With M = 128
+ * the kernels run C = 64 as chunks of 32 (their tiles would not fit in the 160 KB of LDS of
+ * a compute unit).
  * Chunks whose decay over the chunk falls below 2^-100 for some slot (f = -inf, or very
  * strong decay) are evaluated token by token instead of in factored form.
  */
