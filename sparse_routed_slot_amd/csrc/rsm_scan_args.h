@@ -1,0 +1,49 @@
+// rsm_scan_args.h -- launch arguments of the chunk scan (shared by the host launcher and the
+// per-type kernel instantiation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/rsm.h"
+
+namespace rsm {
+
+struct SegArgs {
+    long nC;    // chunks in the sequence
+    int S;      // segments
+    int cps;    // chunks per segment
+    float* dH;  // [B*Hh][S-1][M][Dv]
+    float* dE;  // [B*Hh][S-1][M]
+};
+
+struct ScanArgs {
+    const void *q, *k, *v;
+    const float* H0;
+    long B, T_len, Hh;
+    int Dv, K;
+    SegArgs sg;
+    const unsigned long long* rmask;
+    const float* ralpha;
+    float *o, *H_out;
+    hipStream_t s;
+};
+
+// Between the two passes: dH_s <- H_start(s+1) = diag(E_s) H_start(s) + dH_s for s = 0 .. S-2,
+// H_start(0) = H0 (or zero), so that each segment of pass B reads its start state directly.
+int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream);
+
+// Launch passes A (if S > 1) and B of the chunk scan for one input type and slot count M;
+// C and DT are the chunk length and Dv tile the layout chose.  Each is defined in its own
+// compilation unit (rsm_scan_<type>_m<M>.hip).
+#define RSM_SCAN_DECL(TY, MV) int scan_##TY##_m##MV(int C, int DT, const ScanArgs& a);
+RSM_SCAN_DECL(f32, 16)
+RSM_SCAN_DECL(f32, 32)
+RSM_SCAN_DECL(f32, 64)
+RSM_SCAN_DECL(f32, 128)
+RSM_SCAN_DECL(bf16, 16)
+RSM_SCAN_DECL(bf16, 32)
+RSM_SCAN_DECL(bf16, 64)
+RSM_SCAN_DECL(bf16, 128)
+#undef RSM_SCAN_DECL
+
+}  // namespace rsm
