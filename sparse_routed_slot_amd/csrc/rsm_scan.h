@@ -43,6 +43,11 @@ namespace rsm {
 
 constexpr float kAlphaMin = 9.3576230e-14f;  // e^-30: clamp of alpha on the factored path
 constexpr float kSafeMin = 7.8886091e-31f;   // 2^-100: smallest E_last kept factored
+// Raw buffer resources for the output stores: no stride, range kOutRange bytes from the chunk's
+// first output row (far past any row of a chunk); an offset past it drops the store.
+constexpr int kOutRange = 0x7FFFFF00;
+constexpr int kBufferFlags = 0x00020000;  // dword 3 of a gfx9 buffer resource
+typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -575,9 +580,17 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int EPG = 16 / int(sizeof(T));       // input elements per granule
     constexpr int NTC = C / 16, NTD = DT / 16, NTM = M / 16, NTMP = MP / 16;
     constexpr int NKM = MP / KB, NKC = CP / KB;
-    constexpr int GT = NW / NTD;               // waves per column tile
-    constexpr int NTT = (NTC + GT - 1) / GT;   // output row tiles per wave, at most
-    constexpr int SPW = M / NW;                // slots per wave in the decay-product pass
+    // Wave roles.  Pass B with M <= 64: waves 0-3 own the state columns (MFMA work), waves
+    // 4-7 compute the decay products, so each SIMD runs one of each and their vector and
+    // matrix work overlap.  Otherwise every wave does both.
+    constexpr bool SPLIT = !PASS_A && M <= 64;
+    constexpr int NMW = SPLIT ? 4 : NW;              // state-column (MFMA) waves: 0 .. NMW-1
+    constexpr int NPW = SPLIT ? 4 : NW;              // decay-product waves: PW0 .. NW-1
+    constexpr int PW0 = NW - NPW;
+    constexpr int DPW = NTD > NMW ? NTD / NMW : 1;   // column tiles per MFMA wave
+    constexpr int GT = NTD >= NMW ? 1 : NMW / NTD;   // MFMA waves per column tile
+    constexpr int NTT = (NTC + GT - 1) / GT;         // output row tiles per MFMA wave, at most
+    constexpr int SPW = M / NPW;                     // slots per decay-product wave
     constexpr int MW = (M + 63) / 64;          // 64-bit words of a token's selection mask
     constexpr int NS = NTC * (NTC + 1) / 2;    // lower-triangular tiles of S^T
     constexpr int psQ = CP * QP + 8;           // plane stride of Qh / Kh
@@ -585,7 +598,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int psP = NTC * NKC * 64 * EPL;  // plane stride of the P^T fragments
     constexpr int NWD = SPW * int(sizeof(T)) / 4;  // 32-bit words of a lane's q (or k) piece
-    static_assert(NW % NTD == 0 && SPW >= 2 && SPW <= 16 && C <= 64, "tile split");
+    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPW >= 2 && SPW <= 16 && C <= 64, "tile split");
     static_assert(2 * SZQK * int(sizeof(E)) >= 12 * C * M, "exact-path scratch");
 
     // LDS.  Every array is a separate object so the compiler can tell the direct loads from
@@ -625,8 +638,11 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // EXEC masking around the MFMAs, which would not be skipped lane by lane)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(w >= 0 && w < NW);
-    const int D = w % NTD, g = w / NTD;
-    const int s0 = w * SPW;                         // first slot of this wave's decay products
+    const bool mwave = w < NMW, pwave = w >= PW0;  // roles (both for every wave unless split)
+    const int g = GT == 1 ? 0 : w / NTD;           // MFMA wave: token-tile group
+    // column tile j of an MFMA wave
+    auto Dj = [&](int j) { return GT == 1 ? w + NMW * j : w % NTD; };
+    const int s0 = (w - PW0) * SPW;                // decay-product wave: first slot
     const long rstride = long(Hh);                  // rows between consecutive tokens of one head
     const long segrow = (bh * (sg.S - 1) + seg) * M;  // row of this segment in dH / dE
     auto valid_rows = [&](long c) { return int(T_len - c * C < C ? T_len - c * C : C); };
@@ -671,14 +687,20 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             s.wd[0] = *reinterpret_cast<const uint32_t*>(src);
         }
     };
+    // (lanes past the chunk or the sequence get zeros; they load a valid row and select, so
+    // the pieces are never assigned under a branch and stay in registers)
     auto load_qk = [&](long c, Seg& qs, Seg& ks) {
+        if (!pwave) return;
         const long t = c * C + lane;
-        if (lane < C && t < T_len) {
-            load_piece(kbase + t * rstride * M, ks);
-            if (!PASS_A) load_piece(qbase + t * rstride * M, qs);
-        } else {
+        const bool ok = lane < C && t < T_len;
+        const long row = (ok ? t : 0) * rstride * M;
+        Seg x, y;
+        load_piece(kbase + row, x);
+        if (!PASS_A) load_piece(qbase + row, y);
 #pragma unroll
-            for (int p = 0; p < NWD; ++p) ks.wd[p] = qs.wd[p] = 0u;
+        for (int p = 0; p < NWD; ++p) {
+            ks.wd[p] = ok ? x.wd[p] : 0u;
+            qs.wd[p] = PASS_A ? 0u : ok ? y.wd[p] : 0u;
         }
     };
     auto unpack = [&](const Seg& s, float (&x)[SPW]) {
@@ -728,6 +750,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // factored range.
     auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW]) __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
+        if (!pwave) return;
         E* sQK = NB ? sQK1 : sQK0;
         float al[SPW];
         gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
@@ -752,7 +775,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // one below the factored range
     auto prep_tail = [&](auto nb, const float (&Ev)[SPW]) __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
-        if (lane == 63) {
+        if (pwave && lane == 63) {
             Pol<float>::template put_row<SPW>(NB ? sE1 : sE0, 0, s0, Ev);
             int bad = 0;
 #pragma unroll
@@ -793,10 +816,11 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // ---- the state: Hreg[I][r] = H[16*I + 4*q4 + r][d0 + 16*D + l16]; slot tiles past M
     // (padding of the k-blocks) stay zero.  Pass B starts from H0 (or zero) and folds in the
     // segments before its own; pass A starts from zero.
-    floatx4 Hreg[NTMP];
+    floatx4 Hreg[DPW][NTMP];
 #pragma unroll
-    for (int I = 0; I < NTMP; ++I) Hreg[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int dcol = d0 + 16 * D + l16;
+    for (int j = 0; j < DPW; ++j)
+#pragma unroll
+        for (int I = 0; I < NTMP; ++I) Hreg[j][I] = floatx4{0.f, 0.f, 0.f, 0.f};
     float Eseg = 1.0f;  // pass A: decay product over the segment of slot tid (tid < M)
 
     // LDS padding (slot columns past M, chunk rows past C, P^T fragments above the diagonal)
@@ -810,23 +834,31 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     };
 
     // ---- phase Y, factored path: output tiles, U, state update
-    auto y_phase = [&](auto cur, auto gc, floatx4 (&acc)[NTT]) __attribute__((always_inline)) {
+    auto y_phase = [&](auto cur, auto gc, long c, int nvalid) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur)::value, G = decltype(gc)::value;
         const E* sQK = CUR ? sQK1 : sQK0;
         const T* rvc = CUR ? rv1 : rv0;
         const float* sE = CUR ? sE1 : sE0;
-        frag va[NKC];  // V^T rows of the column tile (k = chunk rows in the order jperm)
+        frag va[DPW][NKC];  // V^T rows of the column tiles (k = chunk rows in the order jperm)
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) va[kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * D, kb, q4, l16);
+        for (int j = 0; j < DPW; ++j)
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                va[j][kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * Dj(j), kb, q4, l16);
         if (!PASS_A) {
-            dfrag hf[NKM];
+            dfrag hf[DPW][NKM];
 #pragma unroll
-            for (int kb = 0; kb < NKM; ++kb) hf[kb] = P::pack_perm(Hreg, kb);
+            for (int j = 0; j < DPW; ++j)
+#pragma unroll
+                for (int kb = 0; kb < NKM; ++kb) hf[j][kb] = P::pack_perm(Hreg[j], kb);
+            // outputs go out by buffer stores whose offset is out of range for rows past the
+            // sequence end (dropped by the hardware), so no branch splits this block
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                o + ((b * T_len + c * C) * rstride + h) * Dv + d0, short(0), kOutRange, kBufferFlags);
             static_for<NTT>([&](auto nc) {
                 constexpr int N = decltype(nc)::value, TT = G + GT * N;
-                acc[N] = floatx4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (TT < NTC) {
-                    dfrag qf[NKM];
+                    dfrag qf[NKM], pf[NKC];  // shared by the wave's column tiles
 #pragma unroll
                     for (int kb = 0; kb < NKM; ++kb)
 #pragma unroll
@@ -834,29 +866,42 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                             qf[kb].p[pl] = P::ld_jrow(sQK, pl * psQ + (16 * TT + l16) * QP, kb, q4);
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
-                        if (kb * KB < 16 * (TT + 1))
-                            acc[N] = P::mm_vd(va[kb], P::template ld_pfrag<NKC>(sP, psP, TT, kb, lane), acc[N]);
+                        if (kb * KB < 16 * (TT + 1)) pf[kb] = P::template ld_pfrag<NKC>(sP, psP, TT, kb, lane);
+                    const int tl = 16 * TT + l16;
 #pragma unroll
-                    for (int kb = 0; kb < NKM; ++kb) acc[N] = P::mm_dd(hf[kb], qf[kb], acc[N]);
+                    for (int j = 0; j < DPW; ++j) {
+                        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < NKC; ++kb)
+                            if (kb * KB < 16 * (TT + 1)) acc = P::mm_vd(va[j][kb], pf[kb], acc);
+#pragma unroll
+                        for (int kb = 0; kb < NKM; ++kb) acc = P::mm_dd(hf[j][kb], qf[kb], acc);
+                        const int off =
+                            tl < nvalid ? int((tl * rstride * Dv + 16 * Dj(j) + 4 * q4) * 4) : kOutRange + 16;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32x4, acc), orsrc, off, 0, 0);
+                    }
                 }
             });
         }
         static_for<NTM>([&](auto ic) {
             constexpr int I = decltype(ic)::value;
-            dfrag kf[NKC];
+            dfrag kf[NKC];  // shared by the wave's column tiles
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
 #pragma unroll
                 for (int pl = 0; pl < NPL; ++pl)
                     kf[kb].p[pl] = P::template ld_col<true>(sQK, oK + pl * psQ + 16 * I, QP, kb, q4, l16);
-            floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) u = P::mm_dv(kf[kb], va[kb], u);
             const float4 e4 = *reinterpret_cast<const float4*>(sE + (16 * I + 4 * q4));
             const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)  // rows of slots untouched in the chunk (E = 1) keep their bits
-                Hreg[I][r] = ev[r] < 1.0f ? ev[r] * (Hreg[I][r] + u[r]) : Hreg[I][r];
+            for (int j = 0; j < DPW; ++j) {
+                floatx4 u = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) u = P::mm_dv(kf[kb], va[j][kb], u);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)  // rows of slots untouched in the chunk (E = 1) keep their bits
+                    Hreg[j][I][r] = ev[r] < 1.0f ? ev[r] * (Hreg[j][I][r] + u[r]) : Hreg[j][I][r];
+            }
         });
     };
 
@@ -870,7 +915,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         float* xk = reinterpret_cast<float*>(CUR ? sQK0 : sQK1);
         float* sE = CUR ? sE1 : sE0;
         const T* rvc = CUR ? rv1 : rv0;
-        {
+        if (pwave) {
             float al[SPW], x[SPW];
             gather(CUR ? rA1 : rA0, CUR ? rM1 : rM0, nvalid, al);
             Seg qs2, ks2;
@@ -890,32 +935,38 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             if (lane == 63) Pol<float>::template put_row<SPW>(sE, 0, s0, x);
         }
         wg_barrier();
-        for (int tt = 0; tt < nvalid; ++tt) {
-            const float vd = Elem<T>::load(rvc, swz_elem<GV, 2, EPG>(tt, 16 * D + l16));
-            float part = 0.0f;
+        if (mwave) {
+            for (int tt = 0; tt < nvalid; ++tt) {
 #pragma unroll
-            for (int I = 0; I < NTM; ++I) {
-                const int i0 = tt * M + 16 * I + 4 * q4;
-                const float4 a4 = *reinterpret_cast<const float4*>(xa + i0);
-                const float4 k4 = *reinterpret_cast<const float4*>(xk + i0);
-                const float av[4] = {a4.x, a4.y, a4.z, a4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
+                for (int j = 0; j < DPW; ++j) {
+                    const float vd = Elem<T>::load(rvc, swz_elem<GV, 2, EPG>(tt, 16 * Dj(j) + l16));
+                    float part = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {  // a select, not a conditional store: Hreg stays in registers
-                    const float hn = fmaf(av[r], Hreg[I][r], (1.0f - av[r]) * kv[r] * vd);
-                    Hreg[I][r] = av[r] != 1.0f ? hn : Hreg[I][r];
+                    for (int I = 0; I < NTM; ++I) {
+                        const int i0 = tt * M + 16 * I + 4 * q4;
+                        const float4 a4 = *reinterpret_cast<const float4*>(xa + i0);
+                        const float4 k4 = *reinterpret_cast<const float4*>(xk + i0);
+                        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {  // a select, not a conditional store: Hreg stays in registers
+                            const float hn = fmaf(av[r], Hreg[j][I][r], (1.0f - av[r]) * kv[r] * vd);
+                            Hreg[j][I][r] = av[r] != 1.0f ? hn : Hreg[j][I][r];
+                        }
+                        if (!PASS_A) {
+                            const float4 x4 = *reinterpret_cast<const float4*>(xa + (C * M + i0));
+                            part = fmaf(x4.x, Hreg[j][I][0], part);
+                            part = fmaf(x4.y, Hreg[j][I][1], part);
+                            part = fmaf(x4.z, Hreg[j][I][2], part);
+                            part = fmaf(x4.w, Hreg[j][I][3], part);
+                        }
+                    }
+                    if (!PASS_A) {
+                        part += __shfl_xor(part, 16);
+                        part += __shfl_xor(part, 32);
+                        if (g == 0 && q4 == 0)
+                            o[((b * T_len + c * C + tt) * rstride + h) * Dv + d0 + 16 * Dj(j) + l16] = part;
+                    }
                 }
-                if (!PASS_A) {
-                    const float4 x4 = *reinterpret_cast<const float4*>(xa + (C * M + i0));
-                    part = fmaf(x4.x, Hreg[I][0], part);
-                    part = fmaf(x4.y, Hreg[I][1], part);
-                    part = fmaf(x4.z, Hreg[I][2], part);
-                    part = fmaf(x4.w, Hreg[I][3], part);
-                }
-            }
-            if (!PASS_A) {
-                part += __shfl_xor(part, 16);
-                part += __shfl_xor(part, 32);
-                if (g == 0 && q4 == 0) o[((b * T_len + c * C + tt) * rstride + h) * Dv + dcol] = part;
             }
         }
         wg_barrier();  // the dense copies are read; the exact sE is written
@@ -935,7 +986,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         const int* sF = CUR ? sF1 : sF0;
         int unsafe = 0;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) unsafe |= sF[i];
+        for (int i = PW0; i < NW; ++i) unsafe |= sF[i];
         unsafe = __builtin_amdgcn_readfirstlane(unsafe);
         if (!PASS_A) {
             if (!unsafe) s_phase(cur);
@@ -957,34 +1008,24 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
             load_qk(c + 2, qn, kn);
             // output tiles, U, the state update and the next chunk's decay products form one
-            // block of code (outputs stored after it), so the compiler can interleave the
-            // MFMA chains with the scan's vector work
-            floatx4 acc[NTT];
-            if constexpr (GT == 1) {
-                y_phase(cur, std::integral_constant<int, 0>{}, acc);
+            // block of code, so the compiler can interleave the MFMA chains with the scan's
+            // vector work
+            if (!mwave) {
+            } else if constexpr (GT == 1) {
+                y_phase(cur, std::integral_constant<int, 0>{}, c, nvalid);
             } else {
                 switch (g) {
-                    case 0: y_phase(cur, std::integral_constant<int, 0>{}, acc); break;
-                    case 1: y_phase(cur, std::integral_constant<int, 1>{}, acc); break;
-                    case 2: if constexpr (GT > 2) y_phase(cur, std::integral_constant<int, 2>{}, acc); break;
-                    case 3: if constexpr (GT > 3) y_phase(cur, std::integral_constant<int, 3>{}, acc); break;
-                    case 4: if constexpr (GT > 4) y_phase(cur, std::integral_constant<int, 4>{}, acc); break;
-                    case 5: if constexpr (GT > 5) y_phase(cur, std::integral_constant<int, 5>{}, acc); break;
-                    case 6: if constexpr (GT > 6) y_phase(cur, std::integral_constant<int, 6>{}, acc); break;
-                    case 7: if constexpr (GT > 7) y_phase(cur, std::integral_constant<int, 7>{}, acc); break;
+                    case 0: y_phase(cur, std::integral_constant<int, 0>{}, c, nvalid); break;
+                    case 1: y_phase(cur, std::integral_constant<int, 1>{}, c, nvalid); break;
+                    case 2: if constexpr (GT > 2) y_phase(cur, std::integral_constant<int, 2>{}, c, nvalid); break;
+                    case 3: if constexpr (GT > 3) y_phase(cur, std::integral_constant<int, 3>{}, c, nvalid); break;
+                    case 4: if constexpr (GT > 4) y_phase(cur, std::integral_constant<int, 4>{}, c, nvalid); break;
+                    case 5: if constexpr (GT > 5) y_phase(cur, std::integral_constant<int, 5>{}, c, nvalid); break;
+                    case 6: if constexpr (GT > 6) y_phase(cur, std::integral_constant<int, 6>{}, c, nvalid); break;
+                    case 7: if constexpr (GT > 7) y_phase(cur, std::integral_constant<int, 7>{}, c, nvalid); break;
                 }
             }
             prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev);
-            if (!PASS_A) {
-                float* obase = o + ((b * T_len + c * C) * rstride + h) * Dv + d0 + 16 * D + 4 * q4;
-#pragma unroll
-                for (int n = 0; n < NTT; ++n) {
-                    const int tl = 16 * (g + GT * n) + l16;
-                    if ((NTC % GT == 0 || g + GT * n < NTC) && tl < nvalid)
-                        *reinterpret_cast<float4*>(obase + tl * rstride * Dv) =
-                            make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-                }
-            }
         }
         prep_tail(std::integral_constant<int, NXT>{}, Ev);
         if (PASS_A && tid < M) Eseg *= (CUR ? sE1 : sE0)[tid];
@@ -1005,11 +1046,13 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         // segment 0 starts from H0 (or zero); segment s > 0 from the state the segments before
         // it leave, folded in place of dH_{s-1} between the two passes
         const float* hs = seg > 0 ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv : H0 ? H0 + bh * M * Dv : nullptr;
-        if (hs) {
+        if (hs && mwave) {
 #pragma unroll
-            for (int I = 0; I < NTM; ++I)
+            for (int j = 0; j < DPW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Hreg[I][r] = hs[(16 * I + 4 * q4 + r) * Dv + dcol];
+                for (int I = 0; I < NTM; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Hreg[j][I][r] = hs[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16];
         }
     }
     if (MP > M || CP > C) zero_qk();
@@ -1027,20 +1070,16 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         if (c + 1 < c_end) chunk(std::integral_constant<int, 1>{}, c + 1);
     }
 
-    if (PASS_A) {
-        if (g == 0) {
+    if (mwave && g == 0 && (PASS_A || (H_out && seg == sg.S - 1))) {
+        float* dst = PASS_A ? sg.dH + segrow * Dv : H_out + bh * M * Dv;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j)
 #pragma unroll
             for (int I = 0; I < NTM; ++I)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sg.dH[(segrow + 16 * I + 4 * q4 + r) * Dv + dcol] = Hreg[I][r];
-        }
-        if (dtile == 0 && tid < M) sg.dE[segrow + tid] = Eseg;
-    } else if (H_out && seg == sg.S - 1 && g == 0) {
-#pragma unroll
-        for (int I = 0; I < NTM; ++I)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) H_out[(bh * M + 16 * I + 4 * q4 + r) * Dv + dcol] = Hreg[I][r];
+                for (int r = 0; r < 4; ++r) dst[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16] = Hreg[j][I][r];
     }
+    if (PASS_A && dtile == 0 && tid < M) sg.dE[segrow + tid] = Eseg;
 }
 
 template <typename T, int M, int C, int DT>
