@@ -650,11 +650,15 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // ---- direct loads of v (rows past the sequence end repeat the last row; their tokens
     // carry no route entries, so they contribute nothing) and of the route
     const long v_pitch = rstride * Dv * long(sizeof(T));
-    TileDma<int(sizeof(rv0)), DT * int(sizeof(T)), NW, 2> dv;
-    dv.init(w, lane, v_pitch);
+    // The direct loads are issued by the decay-product waves only (instruction r by wave
+    // PW0 + r % NPW), right after their last read of the route buffer in a phase: the
+    // compiler then never has a direct load in flight ahead of another wave's LDS reads.
+    const int pw_i = w - PW0;
+    TileDma<int(sizeof(rv0)), DT * int(sizeof(T)), NPW, 2> dv;
+    dv.init(pw_i, lane, v_pitch);
     const T* vbase = v + (b * T_len * rstride + h) * Dv + d0;
     auto issue_v = [&](long c, T* dst) {
-        dv.issue(dst, reinterpret_cast<const char*>(vbase + c * C * rstride * Dv), w, lane, valid_rows(c), v_pitch);
+        dv.issue(dst, reinterpret_cast<const char*>(vbase + c * C * rstride * Dv), pw_i, lane, valid_rows(c), v_pitch);
     };
     const float* abase = ralpha + bh * T_pad * K;
     const unsigned long long* mbase = rmask + bh * T_pad * MW;
@@ -662,8 +666,8 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         const char* ab = reinterpret_cast<const char*>(abase + c * C * K);
         const char* mb = reinterpret_cast<const char*>(mbase + c * C * MW);
         const int na = C * K * 4, nm = C * MW * 8;
-        dma_tile<NW>(dA, pad1k(na), w, lane, [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); });
-        dma_tile<NW>(dM, pad1k(nm), w, lane,
+        dma_tile<NPW>(dA, pad1k(na), pw_i, lane, [&](int off) { return static_cast<const void*>(ab + min(off, na - 16)); });
+        dma_tile<NPW>(dM, pad1k(nm), pw_i, lane,
                      [&](int off) { return static_cast<const void*>(mb + min(off, nm - 16)); });
     };
 
@@ -690,7 +694,6 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // (lanes past the chunk or the sequence get zeros; they load a valid row and select, so
     // the pieces are never assigned under a branch and stay in registers)
     auto load_qk = [&](long c, Seg& qs, Seg& ks) {
-        if (!pwave) return;
         const long t = c * C + lane;
         const bool ok = lane < C && t < T_len;
         const long row = (ok ? t : 0) * rstride * M;
@@ -748,12 +751,14 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // chunk c into buffer NB.  E is an inclusive product scan across the lanes of the clamped
     // alphas.  Also the per-slot E at the chunk end and the flag of a product that left the
     // factored range.
-    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW]) __attribute__((always_inline)) {
+    // mid(): called once the route of chunk c has been read (the direct loads go there)
+    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW], auto&& mid)
+                    __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
-        if (!pwave) return;
         E* sQK = NB ? sQK1 : sQK0;
         float al[SPW];
         gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
+        mid();
 #pragma unroll
         for (int j = 0; j < SPW; ++j) Ev[j] = clamp_alpha(al[j]);
         wave_scan_mul_n<SPW>(Ev);
@@ -775,7 +780,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // one below the factored range
     auto prep_tail = [&](auto nb, const float (&Ev)[SPW]) __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
-        if (pwave && lane == 63) {
+        if (lane == 63) {
             Pol<float>::template put_row<SPW>(NB ? sE1 : sE0, 0, s0, Ev);
             int bad = 0;
 #pragma unroll
@@ -791,7 +796,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         static_for<NS>([&](auto sc) {
             constexpr int S = decltype(sc)::value;
             constexpr int TT = tri_row(S), J = S - TT * (TT + 1) / 2;
-            if (S % NW == w) {
+            if (S % NMW == w) {
                 dfrag a[NKM], bq[NKM];
 #pragma unroll
                 for (int kb = 0; kb < NKM; ++kb)
@@ -909,13 +914,14 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // token-by-token recurrence on the register state with the exact alphas.  Dense fp32
     // alpha [C][M] and q [C][M] go into one Qh/Kh buffer, k [C][M] into the other (neither
     // is in use: this chunk's Qh / Kh are invalid and chunk c+1 is prepared afterwards).
-    auto exact = [&](auto cur, long c, int nvalid) __attribute__((always_inline)) {
+    auto exact = [&](auto cur, long c, int nvalid, auto dm, auto dp) __attribute__((always_inline)) {
+        constexpr bool DM = decltype(dm)::value, DP = decltype(dp)::value;
         constexpr int CUR = decltype(cur)::value;
         float* xa = reinterpret_cast<float*>(CUR ? sQK1 : sQK0);
         float* xk = reinterpret_cast<float*>(CUR ? sQK0 : sQK1);
         float* sE = CUR ? sE1 : sE0;
         const T* rvc = CUR ? rv1 : rv0;
-        if (pwave) {
+        if constexpr (DP) {
             float al[SPW], x[SPW];
             gather(CUR ? rA1 : rA0, CUR ? rM1 : rM0, nvalid, al);
             Seg qs2, ks2;
@@ -935,7 +941,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             if (lane == 63) Pol<float>::template put_row<SPW>(sE, 0, s0, x);
         }
         wg_barrier();
-        if (mwave) {
+        if constexpr (DM) {
             for (int tt = 0; tt < nvalid; ++tt) {
 #pragma unroll
                 for (int j = 0; j < DPW; ++j) {
@@ -976,8 +982,9 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     // pieces of chunk c+1 are in (qc, kc); those of chunk c+2 are loaded into the other pair
     // at the start of phase Y.
     Seg qA, kA, qB, kB;
-    auto chunk = [&](auto cur, long c) __attribute__((always_inline)) {
+    auto chunk = [&](auto cur, long c, auto dm, auto dp) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur)::value, NXT = CUR ^ 1;
+        constexpr bool DM = decltype(dm)::value, DP = decltype(dp)::value;
         const int nvalid = valid_rows(c);
         Seg& qc = CUR ? qB : qA;
         Seg& kc = CUR ? kB : kA;
@@ -989,29 +996,27 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         for (int i = PW0; i < NW; ++i) unsafe |= sF[i];
         unsafe = __builtin_amdgcn_readfirstlane(unsafe);
         if (!PASS_A) {
-            if (!unsafe) s_phase(cur);
+            if constexpr (DM)
+                if (!unsafe) s_phase(cur);
             __builtin_amdgcn_s_waitcnt(0);  // v of chunk c, the route and q / k of c+1 have landed
             wg_barrier();
         }
-        if (c + 1 < c_end) issue_v(c + 1, NXT ? rv1 : rv0);
+        // direct loads of v of chunk c+1 (its buffer was last read in the previous chunk) and
+        // of the route of chunk c+2 (into the buffer chunk c's route was read from)
+        auto issue_next = [&]() {
+            if (c + 1 < c_end) issue_v(c + 1, NXT ? rv1 : rv0);
+            if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
+        };
         float Ev[SPW];
         if (unsafe) {
-            exact(cur, c, nvalid);
-            if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
-            load_qk(c + 2, qn, kn);
+            exact(cur, c, nvalid, dm, dp);
             if (MP > M || CP > C) {
                 zero_qk();
                 wg_barrier();
             }
-            prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev);
-        } else {
-            if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
-            load_qk(c + 2, qn, kn);
-            // output tiles, U, the state update and the next chunk's decay products form one
-            // block of code, so the compiler can interleave the MFMA chains with the scan's
-            // vector work
-            if (!mwave) {
-            } else if constexpr (GT == 1) {
+        } else if constexpr (DM) {
+            // output tiles, U and the state update
+            if constexpr (GT == 1) {
                 y_phase(cur, std::integral_constant<int, 0>{}, c, nvalid);
             } else {
                 switch (g) {
@@ -1025,59 +1030,76 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
                     case 7: if constexpr (GT > 7) y_phase(cur, std::integral_constant<int, 7>{}, c, nvalid); break;
                 }
             }
-            prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev);
         }
-        prep_tail(std::integral_constant<int, NXT>{}, Ev);
+        // decay products and Qh / Kh of chunk c+1, then q / k of chunk c+2 into registers
+        if constexpr (DP) {
+            prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev, issue_next);
+            load_qk(c + 2, qn, kn);
+            prep_tail(std::integral_constant<int, NXT>{}, Ev);
+        }
         if (PASS_A && tid < M) Eseg *= (CUR ? sE1 : sE0)[tid];
         if (PASS_A) __builtin_amdgcn_s_waitcnt(0);  // v of chunk c+1, the route and q / k of c+2 have landed
         wg_barrier();
     };
 
-    // ---- prologue: route, q, k and v of the first chunk in flight while the start state is
-    // loaded and LDS is cleared; then the decay products and Qh / Kh of the first chunk
-    if (c_begin < c_end) {
-        issue_route(c_begin, rA0, rM0);
-        issue_v(c_begin, rv0);
-        load_qk(c_begin, qB, kB);
-        if (c_begin + 1 < c_end) issue_route(c_begin + 1, rA1, rM1);
-        load_qk(c_begin + 1, qA, kA);
-    }
-    if (!PASS_A) {
-        // segment 0 starts from H0 (or zero); segment s > 0 from the state the segments before
-        // it leave, folded in place of dH_{s-1} between the two passes
-        const float* hs = seg > 0 ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv : H0 ? H0 + bh * M * Dv : nullptr;
-        if (hs && mwave) {
+    // ---- the whole walk for one role (or both): the two roles run the same sequence of
+    // barriers; with separate copies of the loop each keeps only its own values live
+    auto run = [&](auto dm, auto dp) __attribute__((always_inline)) {
+        constexpr bool DM = decltype(dm)::value, DP = decltype(dp)::value;
+        // ---- prologue: route, q, k and v of the first chunk in flight while the start state is
+        // loaded and LDS is cleared; then the decay products and Qh / Kh of the first chunk
+        if (DP && c_begin < c_end) {
+            issue_route(c_begin, rA0, rM0);
+            issue_v(c_begin, rv0);
+            load_qk(c_begin, qB, kB);
+            if (c_begin + 1 < c_end) issue_route(c_begin + 1, rA1, rM1);
+            load_qk(c_begin + 1, qA, kA);
+        }
+        if (!PASS_A) {
+            // segment 0 starts from H0 (or zero); segment s > 0 from the state the segments before
+            // it leave, folded in place of dH_{s-1} between the two passes
+            const float* hs = seg > 0 ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv : H0 ? H0 + bh * M * Dv : nullptr;
+            if (DM && hs) {
+#pragma unroll
+                for (int j = 0; j < DPW; ++j)
+#pragma unroll
+                    for (int I = 0; I < NTM; ++I)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Hreg[j][I][r] = hs[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16];
+            }
+        }
+        if (MP > M || CP > C) zero_qk();
+        if (!PASS_A) zero16(sP, int(sizeof(sP)));
+        if (c_begin < c_end) {
+            __builtin_amdgcn_s_waitcnt(0);
+            wg_barrier();  // the loads and the zero fill are done
+            if constexpr (DP) {
+                float Ev[SPW];
+                prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev, [] {});
+                prep_tail(std::integral_constant<int, 0>{}, Ev);
+            }
+            wg_barrier();
+        }
+        for (long c = c_begin; c < c_end; c += 2) {
+            chunk(std::integral_constant<int, 0>{}, c, dm, dp);
+            if (c + 1 < c_end) chunk(std::integral_constant<int, 1>{}, c + 1, dm, dp);
+        }
+
+        if (DM && g == 0 && (PASS_A || (H_out && seg == sg.S - 1))) {
+            float* dst = PASS_A ? sg.dH + segrow * Dv : H_out + bh * M * Dv;
 #pragma unroll
             for (int j = 0; j < DPW; ++j)
 #pragma unroll
                 for (int I = 0; I < NTM; ++I)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Hreg[j][I][r] = hs[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16];
+                    for (int r = 0; r < 4; ++r) dst[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16] = Hreg[j][I][r];
         }
-    }
-    if (MP > M || CP > C) zero_qk();
-    if (!PASS_A) zero16(sP, int(sizeof(sP)));
-    if (c_begin < c_end) {
-        __builtin_amdgcn_s_waitcnt(0);
-        wg_barrier();  // the loads and the zero fill are done
-        float Ev[SPW];
-        prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev);
-        prep_tail(std::integral_constant<int, 0>{}, Ev);
-        wg_barrier();
-    }
-    for (long c = c_begin; c < c_end; c += 2) {
-        chunk(std::integral_constant<int, 0>{}, c);
-        if (c + 1 < c_end) chunk(std::integral_constant<int, 1>{}, c + 1);
-    }
-
-    if (mwave && g == 0 && (PASS_A || (H_out && seg == sg.S - 1))) {
-        float* dst = PASS_A ? sg.dH + segrow * Dv : H_out + bh * M * Dv;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j)
-#pragma unroll
-            for (int I = 0; I < NTM; ++I)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16] = Hreg[j][I][r];
+    };
+    if constexpr (SPLIT) {
+        if (mwave) run(std::true_type{}, std::false_type{});
+        else run(std::false_type{}, std::true_type{});
+    } else {
+        run(std::true_type{}, std::true_type{});
     }
     if (PASS_A && dtile == 0 && tid < M) sg.dE[segrow + tid] = Eseg;
 }
