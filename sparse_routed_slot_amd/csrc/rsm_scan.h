@@ -20,14 +20,15 @@
 //  * route (rsm_route.hip, fully parallel): exact top-K per token-head and alpha, written as
 //    a selection bit mask plus the alphas of the selected slots -- the only intermediate in
 //    memory.
-//  * fwd_scan (one workgroup per (batch, head, Dv tile)): walks the chunks in order with the
-//    fp32 state tile in registers.  The chunk's raw q, k, v tiles and its route arrive in
-//    LDS by direct global->LDS loads issued while the previous chunk computes.  Per chunk
-//    each lane takes one token and each wave a group of slots: the lane gathers its alphas
-//    from the route, the decay products E come from a product scan across the wave's lanes,
-//    and the lane writes its rows of Qh and Kh.  Then the three contractions run on 16x16
-//    MFMA tiles, o is written, and the state is updated.  Rows of slots untouched in a chunk
-//    (E_last == 1) are not written, so they keep their exact bits.
+//  * fwd_scan (one workgroup per (batch, head, Dv tile, sequence segment)): walks the
+//    segment's chunks in order with the fp32 state tile in registers, split by column tiles
+//    among the waves that own them.  The chunk's v tile and its route arrive in LDS by direct
+//    global->LDS loads issued a phase ahead; q and k come into registers.  For the decay
+//    products each lane takes one token and each wave a group of slots: the lane gathers its
+//    alphas from the route, E comes from a product scan across the wave's lanes, and the lane
+//    writes its rows of Qh and Kh.  The contractions run on 16x16 MFMA tiles, o is written,
+//    and the state is updated.  Rows of slots untouched in a chunk (E_last == 1) keep their
+//    exact bits.
 //
 // Overflow guard: 1/E grows with the decay accumulated in a chunk.  On the factored path each
 // alpha is clamped below at e^-30 (~1e-13 instead of 0); a chunk whose decay product falls
@@ -61,7 +62,7 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 //
 // fp32 inputs: fp32 MFMA (16x16x4), every operand a plain float.
 // bf16 inputs: bf16 MFMA (16x16x32).  q, k, v are exact bf16, but the derived operands
-// Qh, Kh, P and the state copy are fp32 values: each is carried as a pair hi + lo of bf16
+// Qh, Kh, P and the state are fp32 values: each is carried as a pair hi + lo of bf16
 // (hi = bf16(x), lo = bf16(x - hi)), ~16 significant bits.  A product of two derived
 // operands takes three MFMAs (hi*hi + hi*lo + lo*hi); V times a derived operand takes two.
 // A single bf16 rounding of a derived operand costs up to 2^-9 of |o| wherever one term
@@ -75,16 +76,13 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // a+12; so lane (a + 4e) addresses row rho(e), columns 4a..4a+3.
 // ------------------------------------------------------------------------------------
 //
-// Swizzled tiles.  The raw q, k and v tiles arrive in LDS by direct loads that fill 16-byte
-// granules in order, so their rows cannot be padded; instead granule g of row `row` (GPR
-// granules per row) sits at granule position row*GPR + swz(row, g), an XOR of g with a
-// function of the row, so that the rows a wave reads at once fall into different banks:
-//  * KIND 1 (q, k: lane = row, one granule each): g ^ ((row / RPB) % GPR);
-//  * KIND 2 (v: 8-byte column pieces of 4 rows and 2 adjacent granules per 16 lanes):
-//    g ^ 2*((row / RPB) % (GPR/2)), which keeps granule pairs together;
-//  * KIND 3 (the state copy: 8-byte column pieces of rows 8*q4 + 0..3 per 16 lanes):
-//    g ^ ((2*(row % 4) + 8*((row / 8) % 2)) % GPR);
-// with RPB = max(1, 16 / GPR) rows per 256-byte bank sweep.
+// Swizzled tiles.  The raw v tile arrives in LDS by direct loads that fill 16-byte granules
+// in order, so its rows cannot be padded; instead granule g of row `row` (GPR granules per
+// row) sits at granule position row*GPR + swz(row, g), an XOR of g with a function of the
+// row, so that the rows a wave reads at once fall into different banks.  KIND 2 (8-byte
+// column pieces of 4 rows and 2 adjacent granules per 16 lanes): g ^ 2*((row / RPB) %
+// (GPR/2)), which keeps granule pairs together, with RPB = max(1, 16 / GPR) rows per
+// 256-byte bank sweep.  KIND 0: no swizzle.
 //
 // Every LDS access is written as one offset from its array (arr + off): the compiler then
 // keeps track of which array each access touches and does not make it wait for the direct
@@ -94,10 +92,9 @@ __device__ __forceinline__ int swz(int row, int g) {
     if constexpr (GPR <= 1 || KIND == 0) {
         return g;
     } else {
+        static_assert(KIND == 2, "swizzle kind");
         constexpr int RPB = GPR >= 16 ? 1 : 16 / GPR;
-        if constexpr (KIND == 1) return g ^ ((row / RPB) % GPR);
-        else if constexpr (KIND == 3) return g ^ ((2 * (row & 3) + 8 * ((row >> 3) & 1)) & (GPR - 1));
-        else if constexpr (GPR >= 4) return g ^ (2 * ((row / RPB) % (GPR / 2)));
+        if constexpr (GPR >= 4) return g ^ (2 * ((row / RPB) % (GPR / 2)));
         else return g;
     }
 }
@@ -130,11 +127,6 @@ template <> struct Pol<float> {
     __device__ static __forceinline__ frag ld_col_swz(const E* arr, int base, int col0, int kb, int q4, int l16) {
         const int row = PERM ? jperm(kb, q4, 0) : inat(kb, q4, 0);
         return arr[base + swz_elem<GPR, KIND, 4>(row, col0 + l16)];
-    }
-    __device__ static __forceinline__ void put(E* arr, int ps, int i, float x) { arr[i] = x; }
-    // 4 consecutive values (16-byte aligned)
-    __device__ static __forceinline__ void put4(E* arr, int ps, int i, float a, float b, float c, float d) {
-        *reinterpret_cast<float4*>(arr + i) = make_float4(a, b, c, d);
     }
     // N consecutive values (N*4 bytes aligned to min(16, N*4))
     template <int N>
@@ -220,18 +212,6 @@ template <> struct Pol<bf16_t> {
         lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
         return __builtin_bit_cast(uint32_t, hi);
     }
-    __device__ static __forceinline__ void put(E* arr, int ps, int i, float x) {
-        uint32_t lo;
-        const uint32_t hi = split2(x, 0.0f, lo);
-        arr[i].bits = uint16_t(hi);
-        arr[ps + i].bits = uint16_t(lo);
-    }
-    __device__ static __forceinline__ void put4(E* arr, int ps, int i, float a, float b, float c, float d) {
-        uint32_t l0, l1;
-        const uint32_t h0 = split2(a, b, l0), h1 = split2(c, d, l1);
-        *reinterpret_cast<uint2*>(arr + i) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(arr + (ps + i)) = make_uint2(l0, l1);
-    }
     // N consecutive values as hi / lo planes (N*2 bytes aligned to min(16, N*2))
     template <int N>
     __device__ static __forceinline__ void put_row(E* arr, int ps, int i, const float (&x)[N]) {
@@ -308,31 +288,7 @@ template <> struct Pol<bf16_t> {
     }
 };
 
-// 16 bytes of input elements -> fp32 values
-__device__ __forceinline__ void unpack16(const uint4& x, float (&v)[8], bf16_t) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        v[2 * p] = __uint_as_float(w[p] << 16);
-        v[2 * p + 1] = __uint_as_float(w[p] & 0xFFFF0000u);
-    }
-}
-__device__ __forceinline__ void unpack16(const uint4& x, float (&v)[8], float) {
-    v[0] = __uint_as_float(x.x);
-    v[1] = __uint_as_float(x.y);
-    v[2] = __uint_as_float(x.z);
-    v[3] = __uint_as_float(x.w);
-}
 
-// f(i) for i = tid, tid + NT, ... below N, with a trip count known at compile time.
-template <int N, int NT, typename F>
-__device__ __forceinline__ void for_each_tid(int tid, F f) {
-#pragma unroll
-    for (int it = 0; it < (N + NT - 1) / NT; ++it) {
-        const int i = tid + NT * it;
-        if (N % NT == 0 || i < N) f(i);
-    }
-}
 
 // Direct global->LDS copy of a chunk tile: wave-instruction r moves LDS bytes
 // [r*1024, r*1024 + 1024) of `lds`, lane l the 16 bytes at r*1024 + 16*l, taken from the
@@ -458,60 +414,6 @@ __device__ __forceinline__ float clamp_alpha(float a) {
     return __int_as_float(max(__float_as_int(a), __float_as_int(kAlphaMin)));
 }
 
-// N consecutive input elements (N*sizeof(T) a multiple of 4 bytes, aligned) -> fp32
-template <int N>
-__device__ __forceinline__ void load_row(const bf16_t* arr, int off, float (&x)[N]) {
-    static_assert(N % 2 == 0, "pairs of bf16");
-    uint32_t wds[N / 2];
-    if constexpr (N % 8 == 0) {
-#pragma unroll
-        for (int g = 0; g < N / 8; ++g) {
-            const uint4 u = *reinterpret_cast<const uint4*>(arr + (off + 8 * g));
-            wds[4 * g] = u.x; wds[4 * g + 1] = u.y; wds[4 * g + 2] = u.z; wds[4 * g + 3] = u.w;
-        }
-    } else if constexpr (N == 4) {
-        const uint2 u = *reinterpret_cast<const uint2*>(arr + off);
-        wds[0] = u.x; wds[1] = u.y;
-    } else {
-        wds[0] = *reinterpret_cast<const uint32_t*>(arr + off);
-    }
-#pragma unroll
-    for (int p = 0; p < N / 2; ++p) {
-        x[2 * p] = __uint_as_float(wds[p] << 16);
-        x[2 * p + 1] = __uint_as_float(wds[p] & 0xFFFF0000u);
-    }
-}
-template <int N>
-__device__ __forceinline__ void load_row(const float* arr, int off, float (&x)[N]) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int g = 0; g < N / 4; ++g) {
-            const float4 u = *reinterpret_cast<const float4*>(arr + (off + 4 * g));
-            x[4 * g] = u.x; x[4 * g + 1] = u.y; x[4 * g + 2] = u.z; x[4 * g + 3] = u.w;
-        }
-    } else {
-#pragma unroll
-        for (int g = 0; g < N / 2; ++g) {
-            const float2 u = *reinterpret_cast<const float2*>(arr + (off + 2 * g));
-            x[2 * g] = u.x; x[2 * g + 1] = u.y;
-        }
-    }
-}
-
-// N consecutive elements of row `row` from column col0 of a swizzled tile (col0 a multiple
-// of min(N, elements per granule)); read granule piece by granule piece
-template <int N, int GPR, int KIND, typename T>
-__device__ __forceinline__ void load_row_swz(const T* arr, int row, int col0, float (&x)[N]) {
-    constexpr int EPG = 16 / int(sizeof(T));
-    constexpr int PE = N < EPG ? N : EPG;  // elements per piece
-#pragma unroll
-    for (int pc = 0; pc < N / PE; ++pc) {
-        float y[PE];
-        load_row<PE>(arr, swz_elem<GPR, KIND, EPG>(row, col0 + pc * PE), y);
-#pragma unroll
-        for (int e = 0; e < PE; ++e) x[pc * PE + e] = y[e];
-    }
-}
 
 
 // ------------------------------------------------------------------------------------
