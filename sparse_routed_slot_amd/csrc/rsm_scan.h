@@ -49,6 +49,9 @@ constexpr float kSafeMin = 7.8886091e-31f;   // 2^-100: smallest E_last kept fac
 constexpr int kOutRange = 0x7FFFFF00;
 constexpr int kBufferFlags = 0x00020000;  // dword 3 of a gfx9 buffer resource
 typedef uint32_t uint32x4 __attribute__((ext_vector_type(4)));
+// Pass B folds up to this many earlier segment states itself; beyond that a separate kernel
+// folds them between the passes.
+constexpr int kFoldMax = 3;
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -957,17 +960,52 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             if (c_begin + 1 < c_end) issue_route(c_begin + 1, rA1, rM1);
             load_qk(c_begin + 1, qA, kA);
         }
-        if (!PASS_A) {
-            // segment 0 starts from H0 (or zero); segment s > 0 from the state the segments before
-            // it leave, folded in place of dH_{s-1} between the two passes
-            const float* hs = seg > 0 ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv : H0 ? H0 + bh * M * Dv : nullptr;
-            if (DM && hs) {
+        if (DM && !PASS_A) {
+            // Segment 0 starts from H0 (or zero).  Segment s > 0 starts from the state the
+            // segments before it leave: with more than kFoldMax + 1 segments it was folded in
+            // place of dH_{s-1} between the two passes; otherwise it is folded here, every
+            // segment's (E, dH) loaded at once.
+            auto at = [&](int j, int I, int r) { return (16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16; };
+            const bool folded = sg.S > kFoldMax + 1;
+            const float* hs = (seg > 0 && folded) ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv
+                                                  : H0 ? H0 + bh * M * Dv : nullptr;
+            if (hs) {
 #pragma unroll
                 for (int j = 0; j < DPW; ++j)
 #pragma unroll
                     for (int I = 0; I < NTM; ++I)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) Hreg[j][I][r] = hs[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16];
+                        for (int r = 0; r < 4; ++r) Hreg[j][I][r] = hs[at(j, I, r)];
+            }
+            // segments per batch of loads: all of them if their (E, dH) values fit in about 144
+            // registers, else one at a time
+            constexpr int FB = NTM * (1 + DPW) * 4 * kFoldMax <= 144 ? kFoldMax : 1;
+            for (int s0 = 0; seg > 0 && !folded && s0 < seg; s0 += FB) {
+                float ev[FB][NTM][4], xv[FB][DPW][NTM][4];
+#pragma unroll
+                for (int sj = 0; sj < FB; ++sj) {
+                    const long sr = (bh * (sg.S - 1) + (s0 + sj < seg ? s0 + sj : 0)) * M;  // a valid segment
+#pragma unroll
+                    for (int I = 0; I < NTM; ++I)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            ev[sj][I][r] = sg.dE[sr + 16 * I + 4 * q4 + r];
+#pragma unroll
+                            for (int j = 0; j < DPW; ++j) xv[sj][j][I][r] = sg.dH[sr * Dv + at(j, I, r)];
+                        }
+                }
+#pragma unroll
+                for (int sj = 0; sj < FB; ++sj)
+#pragma unroll
+                    for (int j = 0; j < DPW; ++j)
+#pragma unroll
+                        for (int I = 0; I < NTM; ++I)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {  // untouched rows keep their bits
+                                const float e = ev[sj][I][r];
+                                const bool use = s0 + sj < seg && e != 1.0f;
+                                Hreg[j][I][r] = use ? fmaf(e, Hreg[j][I][r], xv[sj][j][I][r]) : Hreg[j][I][r];
+                            }
             }
         }
         if (MP > M || CP > C) zero_qk();
@@ -1015,8 +1053,10 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
         hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true>), dim3(unsigned(tiles * (sg.S - 1))), dim3(512), 0, s,
                            q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
-        const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);
-        if (st != RSM_OK) return st;
+        if (sg.S > kFoldMax + 1) {
+            const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);
+            if (st != RSM_OK) return st;
+        }
     }
     hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false>), dim3(unsigned(tiles * sg.S)), dim3(512), 0, s, q, k, v,
                        H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
