@@ -340,6 +340,16 @@ struct TileDma {
     }
 };
 
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt unconstrained): all but the N most recent
+// vector memory instructions of this wave have completed (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Workgroup barrier without a memory fence.  A workgroup-scope release fence would also
 // wait for every direct global->LDS load still in flight; the scan waits for those
 // explicitly, one chunk later.  LDS is coherent inside the workgroup, so each wave's own
@@ -598,7 +608,11 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     };
     // (lanes past the chunk or the sequence get zeros; they load a valid row and select, so
     // the pieces are never assigned under a branch and stay in registers)
+    // number of load instructions load_qk issues
+    constexpr int NQK = (NWD % 4 == 0 ? NWD / 4 : 1) * (PASS_A ? 1 : 2);
     auto load_qk = [&](long c, Seg& qs, Seg& ks) {
+        // after every direct load of the phase: the waits for those skip these NQK loads
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const long t = c * C + lane;
         const bool ok = lane < C && t < T_len;
         const long row = (ok ? t : 0) * rstride * M;
@@ -663,6 +677,9 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         E* sQK = NB ? sQK1 : sQK0;
         float al[SPW];
         gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
+        // q / k of this chunk are in: no later use of them has to wait behind the direct
+        // loads issued next
+        wait_vm<0>();
         mid();
 #pragma unroll
         for (int j = 0; j < SPW; ++j) Ev[j] = clamp_alpha(al[j]);
@@ -694,7 +711,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         }
     };
 
-    // ---- phase X: S^T tiles (J, TT), J <= TT, dealt to the waves round-robin
+    // ---- phase X: S^T tiles (J, TT), J <= TT, dealt to the state waves round-robin
     auto s_phase = [&](auto cur) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur)::value;
         const E* sQK = CUR ? sQK1 : sQK0;
@@ -895,15 +912,20 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
         Seg& kc = CUR ? kB : kA;
         Seg& qn = CUR ? qA : qB;
         Seg& kn = CUR ? kA : kB;
+        // pass B: the decay-product waves' direct loads (v of chunk c, the route of c+1) have
+        // landed before they read LDS; the q / k loads of chunk c+2, issued last, may still be
+        // in flight.  (Pass A waits at the end of the previous chunk.)
+        if constexpr (DP && !PASS_A) wait_vm<NQK>();
         const int* sF = CUR ? sF1 : sF0;
         int unsafe = 0;
 #pragma unroll
         for (int i = PW0; i < NW; ++i) unsafe |= sF[i];
         unsafe = __builtin_amdgcn_readfirstlane(unsafe);
         if (!PASS_A) {
+            // (the state waves: the decay-product waves' LDS reads here would wait for their
+            // own q / k loads of chunk c+2)
             if constexpr (DM)
                 if (!unsafe) s_phase(cur);
-            __builtin_amdgcn_s_waitcnt(0);  // v of chunk c, the route and q / k of c+1 have landed
             wg_barrier();
         }
         // direct loads of v of chunk c+1 (its buffer was last read in the previous chunk) and
@@ -943,7 +965,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             prep_tail(std::integral_constant<int, NXT>{}, Ev);
         }
         if (PASS_A && tid < M) Eseg *= (CUR ? sE1 : sE0)[tid];
-        if (PASS_A) __builtin_amdgcn_s_waitcnt(0);  // v of chunk c+1, the route and q / k of c+2 have landed
+        if (PASS_A) wait_vm<NQK>();  // v of chunk c+1 and the route of c+2 have landed
         wg_barrier();
     };
 
