@@ -440,7 +440,7 @@ __device__ __forceinline__ float clamp_alpha(float a) {
 // ------------------------------------------------------------------------------------
 
 // ------------------------------------------------------------------------------------
-// Chunk scan: one workgroup (8 waves) per (b, h, Dv tile of DT columns, segment); it walks
+// Chunk scan: one workgroup (8 or 16 waves) per (b, h, Dv tile of DT columns, segment); it walks
 // the segment's chunks in order.
 //
 // The fp32 state tile stays in registers, split by column tiles: wave w owns column tile
@@ -476,8 +476,13 @@ constexpr int tri_row(int s) {
     return r;
 }
 
+// Waves per workgroup: 16 for pass B with M <= 64 (8 state waves and 8 decay-product waves,
+// two of each per SIMD), else 8.
+template <bool PASS_A, int M>
+constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
+
 template <typename T, int M, int C, int DT, bool PASS_A>
-__global__ __launch_bounds__(512) void fwd_scan_kernel(
+__global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
     long T_len, int Hh, int Dv, int K, SegArgs sg, const unsigned long long* __restrict__ rmask,
     const float* __restrict__ ralpha, float* __restrict__ o, float* __restrict__ H_out) {
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     typedef typename P::E E;
     typedef typename P::frag frag;
     typedef typename P::dfrag dfrag;
-    constexpr int NW = 8, NT = 64 * NW;
+    constexpr int NW = scan_waves<PASS_A, M>(), NT = 64 * NW;
     constexpr int KB = P::KB, EPL = P::EPL, NPL = P::NPL;
     constexpr int MP = M > KB ? M : KB;        // padded slot dimension (k of slot contractions)
     constexpr int CP = C > KB ? C : KB;        // padded chunk dimension (k of row contractions)
@@ -495,12 +500,13 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int EPG = 16 / int(sizeof(T));       // input elements per granule
     constexpr int NTC = C / 16, NTD = DT / 16, NTM = M / 16, NTMP = MP / 16;
     constexpr int NKM = MP / KB, NKC = CP / KB;
-    // Wave roles.  Pass B with M <= 64: waves 0-3 own the state columns (MFMA work), waves
-    // 4-7 compute the decay products, so each SIMD runs one of each and their vector and
-    // matrix work overlap.  Otherwise every wave does both.
+    // Wave roles.  Pass B with M <= 64: the first half of the waves own the state columns
+    // (MFMA work), the second half compute the decay products; wave w runs on SIMD w % 4, so
+    // each SIMD runs both kinds and their vector and matrix work overlap.
+    // Otherwise every wave does both.
     constexpr bool SPLIT = !PASS_A && M <= 64;
-    constexpr int NMW = SPLIT ? 4 : NW;              // state-column (MFMA) waves: 0 .. NMW-1
-    constexpr int NPW = SPLIT ? 4 : NW;              // decay-product waves: PW0 .. NW-1
+    constexpr int NMW = SPLIT ? NW / 2 : NW;         // state-column (MFMA) waves: 0 .. NMW-1
+    constexpr int NPW = SPLIT ? NW / 2 : NW;         // decay-product waves: PW0 .. NW-1
     constexpr int PW0 = NW - NPW;
     constexpr int DPW = NTD > NMW ? NTD / NMW : 1;   // column tiles per MFMA wave
     constexpr int GT = NTD >= NMW ? 1 : NMW / NTD;   // MFMA waves per column tile
@@ -513,7 +519,8 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int psP = NTC * NKC * 64 * EPL;  // plane stride of the P^T fragments
     constexpr int NWD = SPW * int(sizeof(T)) / 4;  // 32-bit words of a lane's q (or k) piece
-    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPW >= 2 && SPW <= 16 && C <= 64, "tile split");
+    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPW >= 2 && SPW <= 16 && C <= 64 && NMW <= 8,
+                  "tile split");
     static_assert(2 * SZQK * int(sizeof(E)) >= 12 * C * M, "exact-path scratch");
 
     // LDS.  Every array is a separate object so the compiler can tell the direct loads from
@@ -1001,7 +1008,7 @@ __global__ __launch_bounds__(512) void fwd_scan_kernel(
             }
             // segments per batch of loads: all of them if their (E, dH) values fit in about 144
             // registers, else one at a time
-            constexpr int FB = NTM * (1 + DPW) * 4 * kFoldMax <= 144 ? kFoldMax : 1;
+            constexpr int FB = NTM * (1 + DPW) * 4 * kFoldMax <= (NW > 8 ? 64 : 144) ? kFoldMax : 1;
             for (int s0 = 0; seg > 0 && !folded && s0 < seg; s0 += FB) {
                 float ev[FB][NTM][4], xv[FB][DPW][NTM][4];
 #pragma unroll
@@ -1072,7 +1079,8 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
                        float* H_out, hipStream_t s) {
     const long tiles = B * Hh * (Dv / DT);
     if (sg.S > 1) {
-        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true>), dim3(unsigned(tiles * (sg.S - 1))), dim3(512), 0, s,
+        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true>), dim3(unsigned(tiles * (sg.S - 1))),
+                           dim3(64 * scan_waves<true, M>()), 0, s,
                            q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
         if (sg.S > kFoldMax + 1) {
@@ -1080,7 +1088,8 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
             if (st != RSM_OK) return st;
         }
     }
-    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false>), dim3(unsigned(tiles * sg.S)), dim3(512), 0, s, q, k, v,
+    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false>), dim3(unsigned(tiles * sg.S)),
+                       dim3(64 * scan_waves<false, M>()), 0, s, q, k, v,
                        H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
