@@ -215,8 +215,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel pass A + "
-                               "seg_fold_kernel + fwd_scan_kernel pass B (four launches back to back on the "
-                               "caller's stream)",
+                               "fwd_scan_kernel pass B (three launches back to back on the caller's stream; "
+                               "the segment fold runs inside pass B at 4 segments)",
                      "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
