@@ -31,6 +31,21 @@
  *
  * Layouts (row-major, contiguous): q,k,z [B,T,Hh,M]; v [B,T,Hh,Dv]; f [B,T,Hh];
  * H0/H_out [B,Hh,M,Dv]; o [B,T,Hh,Dv]; idx [B,T,Hh,K] (ascending slot order).
+ *
+ * Router and decay variants (the *_ex entry points), each named on the pages:
+ *  - score kind: sigmoid (default) or softmax over all M slots (README configuration
+ *    table "top-k sigmoid/softmax" and the router_score option; paper summary section
+ *    6.2.1).  The softmax is increasing in each logit, so the selection is the same top-K
+ *    of the logits; the selected slots take softmax(z)_i = exp(z_i - max z) / sum_j
+ *    exp(z_j - max z).
+ *  - normalize: the selected scores divided by their sum, so they sum to one over the K
+ *    selected slots (paper summary section 4.1).  A zero sum leaves them as they are.
+ *  - per-slot decay: f [B,T,Hh,M], alpha_i = exp(s_i * f_i) (the GLA decay option of the
+ *    README configuration table is a diagonal gate, paper summary section 2.1).
+ *  - exploration noise: g [B,T,Hh,M] added to the logits before selection and scoring
+ *    (paper summary section 6.2.2, Gumbel noise during training).  The caller draws g.
+ *    The noisy logit is the fp32 sum fl32(z + g) -- the precision in which the GPU path
+ *    forms it -- so both sides rank the same numbers.
  */
 #include <math.h>
 #include <stdint.h>
@@ -53,18 +68,56 @@ static void oracle_select(const double* z, long M, long K, unsigned char* sel) {
 
 static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* One token on the columns [c0, c1) of one head's state H [M, Dv]. */
-static void oracle_token(const double* q, const double* k, const double* z, const double* v,
-                         double f, double* H, long M, long Dv, long K, long c0, long c1,
-                         double* o, int32_t* idx, unsigned char* sel) {
-    oracle_select(z, M, K, sel);
+/* Router variant: score kind (0 sigmoid, 1 softmax) and whether the selected scores are
+ * divided by their sum. */
+typedef struct {
+    int softmax;
+    int normalize;
+} oracle_router;
+
+/* Logits of one row as the router ranks them: z, or fl32(z + g) with exploration noise. */
+static void oracle_logits(const double* z, const double* g, long M, double* zp) {
+    for (long i = 0; i < M; ++i) zp[i] = g ? (double)((float)z[i] + (float)g[i]) : z[i];
+}
+
+/* Selection flags and the score of every selected slot (s[i] for sel[i]; 0 elsewhere). */
+static void oracle_route_row(const double* zp, long M, long K, oracle_router r, unsigned char* sel,
+                             double* s) {
+    oracle_select(zp, M, K, sel);
+    double zmax = zp[0], den = 0.0;
+    if (r.softmax) {
+        for (long i = 1; i < M; ++i) zmax = zp[i] > zmax ? zp[i] : zmax;
+        for (long i = 0; i < M; ++i) den += exp(zp[i] - zmax);
+    }
+    double tot = 0.0;
+    for (long i = 0; i < M; ++i) {
+        s[i] = 0.0;
+        if (!sel[i]) continue;
+        s[i] = r.softmax ? exp(zp[i] - zmax) / den : oracle_sigmoid(zp[i]);
+        tot += s[i];
+    }
+    if (r.normalize && tot > 0.0)
+        for (long i = 0; i < M; ++i) s[i] /= tot;
+}
+
+/* One token on the columns [c0, c1) of one head's state H [M, Dv].  f holds one decay
+ * rate (fstride 0) or one per slot (fstride 1); g is the noise row or NULL; w is scratch
+ * of 2*M doubles. */
+static void oracle_token(const double* q, const double* k, const double* z, const double* g,
+                         const double* v, const double* f, long fstride, oracle_router r,
+                         double* H, long M, long Dv, long K, long c0, long c1, double* o,
+                         int32_t* idx, unsigned char* sel, double* w) {
+    double* zp = w;
+    double* sc = w + M;
+    oracle_logits(z, g, M, zp);
+    oracle_route_row(zp, M, K, r, sel, sc);
     long n = 0;
     for (long i = 0; i < M; ++i) {
         if (!sel[i]) continue;
         if (idx) idx[n] = (int32_t)i;
         n++;
-        double s = oracle_sigmoid(z[i]);
-        double alpha = (s == 0.0) ? 1.0 : exp(s * f);
+        double s = sc[i];
+        double alpha = (s == 0.0) ? 1.0 : exp(s * f[i * fstride]);
         if (alpha == 1.0) continue; /* frozen */
         double w = (1.0 - alpha) * k[i];
         double* row = H + i * Dv;
@@ -77,33 +130,45 @@ static void oracle_token(const double* q, const double* k, const double* z, cons
     }
 }
 
-/* Router alone: idx [N,K] ascending slot order, score [N,K] = sigmoid(z) (nullable). */
-int rsm_oracle_route_topk(const double* z, long N, long M, long K, int32_t* idx, double* score) {
+/* Router alone: idx [N,K] ascending slot order, score [N,K] (nullable) = the routing
+ * weight of each selected slot.  noise [N,M] or NULL; softmax, normalize as above. */
+int rsm_oracle_route_ex(const double* z, const double* noise, long N, long M, long K, int softmax,
+                        int normalize, int32_t* idx, double* score) {
     if (!z || !idx || N < 0 || M < 1 || K < 1 || K > M) return -1;
     unsigned char* sel = (unsigned char*)malloc((size_t)M);
-    if (!sel) return -2;
+    double* w = (double*)malloc(sizeof(double) * (size_t)(2 * M));
+    if (!sel || !w) { free(sel); free(w); return -2; }
+    oracle_router rr = {softmax != 0, normalize != 0};
     for (long r = 0; r < N; ++r) {
-        const double* zr = z + r * M;
-        oracle_select(zr, M, K, sel);
+        oracle_logits(z + r * M, noise ? noise + r * M : NULL, M, w);
+        oracle_route_row(w, M, K, rr, sel, w + M);
         long n = 0;
         for (long i = 0; i < M; ++i) {
             if (!sel[i]) continue;
             idx[r * K + n] = (int32_t)i;
-            if (score) score[r * K + n] = oracle_sigmoid(zr[i]);
+            if (score) score[r * K + n] = w[M + i];
             n++;
         }
     }
     free(sel);
+    free(w);
     return 0;
 }
 
+int rsm_oracle_route_topk(const double* z, long N, long M, long K, int32_t* idx, double* score) {
+    return rsm_oracle_route_ex(z, NULL, N, M, K, 0, 0, idx, score);
+}
+
 /* Whole-sequence recurrence.  H0 may be NULL (zero state).  H_out, idx_out may be NULL.
- * H_trace (nullable) receives the state after every token: [B,Hh,T,M,Dv]. */
-int rsm_oracle_forward(const double* q, const double* k, const double* z, const double* v,
-                       const double* f, const double* H0, long B, long T, long Hh, long M,
-                       long Dv, long K, double* o, double* H_out, int32_t* idx_out,
-                       double* H_trace, int nthreads) {
+ * H_trace (nullable) receives the state after every token: [B,Hh,T,M,Dv].
+ * noise [B,T,Hh,M] or NULL; f is [B,T,Hh] (f_per_slot 0) or [B,T,Hh,M] (f_per_slot 1). */
+int rsm_oracle_forward_ex(const double* q, const double* k, const double* z, const double* noise,
+                          const double* v, const double* f, int f_per_slot, const double* H0,
+                          long B, long T, long Hh, long M, long Dv, long K, int softmax,
+                          int normalize, double* o, double* H_out, int32_t* idx_out,
+                          double* H_trace, int nthreads) {
     if (!q || !k || !z || !v || !f || !o) return -1;
+    const oracle_router rr = {softmax != 0, normalize != 0};
     if (B < 1 || T < 0 || Hh < 1 || M < 1 || Dv < 1 || K < 1 || K > M) return -1;
     long ncb = 1;
     if (B * Hh < 64) ncb = Dv >= 8 ? 8 : Dv; /* split columns when heads are few */
@@ -120,8 +185,9 @@ int rsm_oracle_forward(const double* q, const double* k, const double* z, const 
         double* H = (double*)malloc(sizeof(double) * (size_t)(M * Dv));
         unsigned char* sel = (unsigned char*)malloc((size_t)M);
         double* orow = (double*)malloc(sizeof(double) * (size_t)Dv);
-        if (!H || !sel || !orow) {
-            free(H); free(sel); free(orow);
+        double* w = (double*)malloc(sizeof(double) * (size_t)(2 * M));
+        if (!H || !sel || !orow || !w) {
+            free(H); free(sel); free(orow); free(w);
             status = -2;
             continue;
         }
@@ -131,8 +197,9 @@ int rsm_oracle_forward(const double* q, const double* k, const double* z, const 
         for (long t = 0; t < T; ++t) {
             long row = (b * T + t) * Hh + h; /* token-head row index */
             int32_t* idx = (idx_out && cb == 0) ? idx_out + row * K : NULL;
-            oracle_token(q + row * M, k + row * M, z + row * M, v + row * Dv, f[row], H, M, Dv,
-                         K, c0, c1, orow, idx, sel);
+            oracle_token(q + row * M, k + row * M, z + row * M, noise ? noise + row * M : NULL,
+                         v + row * Dv, f_per_slot ? f + row * M : f + row, f_per_slot ? 1 : 0, rr,
+                         H, M, Dv, K, c0, c1, orow, idx, sel, w);
             for (long c = c0; c < c1; ++c) o[row * Dv + c] = orow[c];
             if (H_trace) {
                 double* dst = H_trace + (((b * Hh + h) * T + t) * M) * Dv;
@@ -144,17 +211,28 @@ int rsm_oracle_forward(const double* q, const double* k, const double* z, const 
             for (long i = 0; i < M; ++i)
                 for (long c = c0; c < c1; ++c)
                     H_out[((b * Hh + h) * M + i) * Dv + c] = H[i * Dv + c];
-        free(H); free(sel); free(orow);
+        free(H); free(sel); free(orow); free(w);
     }
     return status;
 }
 
-/* One decode step for every (b, h): q,k,z [B,Hh,M], v [B,Hh,Dv], f [B,Hh];
- * H [B,Hh,M,Dv] updated in place; o [B,Hh,Dv]; idx_out [B,Hh,K] nullable. */
-int rsm_oracle_decode_step(const double* q, const double* k, const double* z, const double* v,
-                           const double* f, double* H, long B, long Hh, long M, long Dv, long K,
-                           double* o, int32_t* idx_out, int nthreads) {
+int rsm_oracle_forward(const double* q, const double* k, const double* z, const double* v,
+                       const double* f, const double* H0, long B, long T, long Hh, long M,
+                       long Dv, long K, double* o, double* H_out, int32_t* idx_out,
+                       double* H_trace, int nthreads) {
+    return rsm_oracle_forward_ex(q, k, z, NULL, v, f, 0, H0, B, T, Hh, M, Dv, K, 0, 0, o, H_out,
+                                 idx_out, H_trace, nthreads);
+}
+
+/* One decode step for every (b, h): q,k,z [B,Hh,M], v [B,Hh,Dv], f [B,Hh] (or [B,Hh,M]
+ * with f_per_slot); noise [B,Hh,M] or NULL; H [B,Hh,M,Dv] updated in place; o [B,Hh,Dv];
+ * idx_out [B,Hh,K] nullable. */
+int rsm_oracle_decode_ex(const double* q, const double* k, const double* z, const double* noise,
+                         const double* v, const double* f, int f_per_slot, double* H, long B,
+                         long Hh, long M, long Dv, long K, int softmax, int normalize, double* o,
+                         int32_t* idx_out, int nthreads) {
     if (!q || !k || !z || !v || !f || !H || !o) return -1;
+    const oracle_router rr = {softmax != 0, normalize != 0};
     if (B < 1 || Hh < 1 || M < 1 || Dv < 1 || K < 1 || K > M) return -1;
     int status = 0;
 #ifdef _OPENMP
@@ -163,12 +241,22 @@ int rsm_oracle_decode_step(const double* q, const double* k, const double* z, co
 #endif
     for (long bh = 0; bh < B * Hh; ++bh) {
         unsigned char* sel = (unsigned char*)malloc((size_t)M);
-        if (!sel) { status = -2; continue; }
-        oracle_token(q + bh * M, k + bh * M, z + bh * M, v + bh * Dv, f[bh], H + bh * M * Dv,
-                     M, Dv, K, 0, Dv, o + bh * Dv, idx_out ? idx_out + bh * K : NULL, sel);
+        double* w = (double*)malloc(sizeof(double) * (size_t)(2 * M));
+        if (!sel || !w) { free(sel); free(w); status = -2; continue; }
+        oracle_token(q + bh * M, k + bh * M, z + bh * M, noise ? noise + bh * M : NULL, v + bh * Dv,
+                     f_per_slot ? f + bh * M : f + bh, f_per_slot ? 1 : 0, rr, H + bh * M * Dv, M,
+                     Dv, K, 0, Dv, o + bh * Dv, idx_out ? idx_out + bh * K : NULL, sel, w);
         free(sel);
+        free(w);
     }
     return status;
+}
+
+int rsm_oracle_decode_step(const double* q, const double* k, const double* z, const double* v,
+                           const double* f, double* H, long B, long Hh, long M, long Dv, long K,
+                           double* o, int32_t* idx_out, int nthreads) {
+    return rsm_oracle_decode_ex(q, k, z, NULL, v, f, 0, H, B, Hh, M, Dv, K, 0, 0, o, idx_out,
+                                nthreads);
 }
 
 int rsm_oracle_max_threads(void) {

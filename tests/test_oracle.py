@@ -289,6 +289,128 @@ class TestInvariants:
         assert np.array_equal(o1, o8) and np.array_equal(H1, H8)
 
 
+def _route_variant_np(zp, K, score, normalize):
+    """Independent routing of one row of (already noisy) logits: selection by a full sort,
+    sigmoid or softmax over all slots, optional renormalisation over the selected slots.
+    Returns (selected slot list ascending, weight per slot [M] with zeros elsewhere)."""
+    M = len(zp)
+    sel = _topk_by_sort(list(zp), K)
+    w = np.zeros(M)
+    if score == "softmax":
+        e = np.exp(zp - zp.max())
+        w[sel] = e[sel] / e.sum()
+    else:
+        w[sel] = _sigmoid(zp[sel])
+    if normalize and w.sum() > 0.0:
+        w = w / w[sel].sum()
+    return sel, w
+
+
+def _step_np(H, q, k, zp, v, f, K, score, normalize):
+    """One token of one head: route, per-slot (or scalar) decay, update, read."""
+    sel, w = _route_variant_np(zp, K, score, normalize)
+    fv = np.broadcast_to(np.asarray(f, dtype=np.float64), zp.shape)
+    H = H.copy()
+    for i in sel:
+        a = 1.0 if w[i] == 0.0 else math.exp(w[i] * fv[i])
+        if a != 1.0:
+            H[i] = a * H[i] + (1.0 - a) * k[i] * v
+    return H, q @ H, sel
+
+
+# ------------------------------------------------------ router and decay variants
+class TestVariants:
+    """Router and decay variants named on the pages: softmax scores (README configuration
+    table and router_score option; paper summary section 6.2.1), renormalised selected
+    weights (paper summary section 4.1), a per-slot decay rate (GLA diagonal gate, README
+    configuration table; paper summary section 2.1) and caller-drawn exploration noise added
+    to the logits (paper summary section 6.2.2)."""
+
+    def test_softmax_two_slots_closed_form(self):
+        a, b = 0.7, -1.3
+        idx, sc = oracle.route_topk(np.array([[a, b]]), 2, score="softmax")
+        assert idx.tolist() == [[0, 1]]
+        np.testing.assert_allclose(sc[0], [1.0 / (1.0 + math.exp(b - a)), 1.0 / (1.0 + math.exp(a - b))],
+                                   rtol=1e-15)
+        idx, sc = oracle.route_topk(np.array([[a, b]]), 1, score="softmax")
+        assert idx.tolist() == [[0]] and abs(sc[0, 0] - 1.0 / (1.0 + math.exp(b - a))) < 1e-15
+
+    def test_softmax_scores_sum_to_one_over_all_slots(self):
+        z = np.random.default_rng(30).standard_normal((50, 16)) * 3.0
+        _, sc = oracle.route_topk(z, 16, score="softmax")
+        np.testing.assert_allclose(sc.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        idx, _ = oracle.route_topk(z, 5, score="softmax")
+        for r in range(len(z)):
+            assert idx[r].tolist() == _topk_by_sort(list(z[r]), 5)
+
+    @pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+    def test_normalized_weights_sum_to_one_and_keep_ratios(self, score):
+        z = np.random.default_rng(31).standard_normal((40, 32)) * 2.0
+        idx, raw = oracle.route_topk(z, 6, score=score)
+        idx2, nrm = oracle.route_topk(z, 6, score=score, normalize=True)
+        assert np.array_equal(idx, idx2)
+        np.testing.assert_allclose(nrm.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(nrm[:, 1:] / nrm[:, :1], raw[:, 1:] / raw[:, :1], rtol=1e-13)
+        if score == "sigmoid":
+            np.testing.assert_allclose(raw, _sigmoid(np.take_along_axis(z, idx, axis=1)), rtol=1e-15)
+
+    def test_noise_is_an_fp32_shift_of_the_logits(self):
+        rng = np.random.default_rng(32)
+        z = rng.standard_normal((64, 16)).astype(np.float32).astype(np.float64)
+        g = -np.log(-np.log(rng.uniform(1e-6, 1.0, (64, 16)))).astype(np.float32).astype(np.float64)
+        zp = (z.astype(np.float32) + g.astype(np.float32)).astype(np.float64)  # numpy fp32 add
+        idx, sc = oracle.route_topk(z, 4, noise=g)
+        for r in range(len(z)):
+            assert idx[r].tolist() == _topk_by_sort(list(zp[r]), 4)
+        np.testing.assert_allclose(sc, _sigmoid(np.take_along_axis(zp, idx, axis=1)), rtol=1e-15)
+        # a shift that flips the winner
+        idx, _ = oracle.route_topk(np.array([[1.0, 0.5]]), 1, noise=np.array([[0.0, 0.75]]))
+        assert idx.tolist() == [[1]]
+
+    def test_per_slot_decay_constant_across_slots_equals_scalar(self):
+        B, T, Hh, M, Dv, K = 1, 30, 2, 8, 5, 3
+        q, k, z, v, f = _rand_f64(B, T, Hh, M, Dv, seed=33)
+        o1, H1, i1 = oracle.forward(q, k, z, v, f, K)
+        fs = np.repeat(f[..., None], M, axis=-1)
+        o2, H2, i2 = oracle.forward(q, k, z, v, fs, K)
+        assert np.array_equal(o1, o2) and np.array_equal(H1, H2) and np.array_equal(i1, i2)
+
+    @pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+    @pytest.mark.parametrize("normalize", [False, True])
+    def test_forward_and_decode_brute_force(self, score, normalize):
+        """Token-by-token recurrence written out here with every variant on: fp32-noisy
+        logits, per-slot decay rates (one of them -inf), sigmoid or softmax, renormalised or
+        not; the decode step continues the same sequence."""
+        B, T, Hh, M, Dv, K = 1, 24, 2, 6, 3, 3
+        q, k, z, v, _ = _rand_f64(B, T, Hh, M, Dv, seed=34)
+        rng = np.random.default_rng(35)
+        fs = -np.log1p(np.exp(rng.standard_normal((B, T, Hh, M))))
+        fs[0, 5, 1, 2] = -np.inf
+        g = rng.gumbel(size=(B, T, Hh, M)).astype(np.float32).astype(np.float64)
+        z = z.astype(np.float32).astype(np.float64)
+        H0 = rng.standard_normal((B, Hh, M, Dv))
+        o, H, idx = oracle.forward(q, k, z, v, fs, K, H0=H0, noise=g, score=score, normalize=normalize)
+        for h in range(Hh):
+            S = H0[0, h].copy()
+            for t in range(T):
+                zp = (z[0, t, h].astype(np.float32) + g[0, t, h].astype(np.float32)).astype(np.float64)
+                S, out, sel = _step_np(S, q[0, t, h], k[0, t, h], zp, v[0, t, h], fs[0, t, h], K, score, normalize)
+                assert idx[0, t, h].tolist() == sel
+                np.testing.assert_allclose(o[0, t, h], out, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(H[0, h], S, rtol=1e-12, atol=1e-13)
+        # one decode step from the final state
+        qd, kd, zd, vd = q[:, 0], k[:, 0], z[:, 1], v[:, 2]
+        fd, gd = fs[:, 3], g[:, 4]
+        Hd = H.copy()
+        od, idd = oracle.decode_step(qd, kd, zd, vd, fd, Hd, K, noise=gd, score=score, normalize=normalize)
+        for h in range(Hh):
+            zp = (zd[0, h].astype(np.float32) + gd[0, h].astype(np.float32)).astype(np.float64)
+            S, out, sel = _step_np(H[0, h], qd[0, h], kd[0, h], zp, vd[0, h], fd[0, h], K, score, normalize)
+            assert idd[0, h].tolist() == sel
+            np.testing.assert_allclose(od[0, h], out, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(Hd[0, h], S, rtol=1e-12, atol=1e-13)
+
+
 class TestGenerator:
     def test_bf16_round_trip_and_rounding(self):
         x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, np.inf, 3.0e38],
