@@ -126,6 +126,53 @@ int rsm_decode_step(const void* q, const void* k, const void* z, const void* v, 
                     const float* f, float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv,
                     int64_t K, float* o, int32_t* idx_out, void* stream);
 
+/*
+ * Router and decay variants, each named on the pages.  The *_ex entry points take one;
+ * NULL, or a zero-initialised struct, is the default router of the entry points above
+ * (and runs the same kernels).
+ *  - score = RSM_SCORE_SOFTMAX: softmax over all M logits instead of the sigmoid (README
+ *    configuration table, "top-k sigmoid/softmax", and its router_score option; paper
+ *    summary section 6.2.1).  The softmax increases with each logit, so the same K slots
+ *    are selected; slot i takes exp(z_i - max z) / sum_j exp(z_j - max z).
+ *  - normalize = 1: the selected scores are divided by their sum, which then is one (paper
+ *    summary section 4.1).  A zero sum leaves them unchanged.
+ *  - f_per_slot = 1: f holds one decay rate per slot, shape [.., M] instead of [..] (the
+ *    GLA decay option of the README configuration table, a diagonal gate; paper summary
+ *    section 2.1): alpha_i = exp(s_i * f_i).  Ignored by rsm_route_topk_ex.
+ *  - noise != NULL: fp32 device buffer shaped like z, added to the logits before selection
+ *    and scoring as an fp32 sum (Gumbel exploration noise during training, paper summary
+ *    section 6.2.2; the caller draws it).  It must not overlap an output.
+ * A field outside {0, 1} (score outside the enum) returns RSM_ERR_UNSUPPORTED.
+ */
+typedef enum { RSM_SCORE_SIGMOID = 0, RSM_SCORE_SOFTMAX = 1 } rsm_score_kind;
+
+typedef struct {
+    int score;          /* rsm_score_kind */
+    int normalize;      /* 0 or 1 */
+    int f_per_slot;     /* 0: f [.., 1 per token-head]; 1: f [.., M] */
+    const float* noise; /* NULL or fp32 [.., M], device memory, read only */
+} rsm_router_opts;
+
+/* rsm_route_topk with a router variant; score (nullable) receives the routing weight of
+ * each selected slot after the softmax / renormalisation. */
+int rsm_route_topk_ex(const void* z, int dtype, const rsm_router_opts* opts, int64_t B, int64_t T,
+                      int64_t Hh, int64_t M, int64_t K, int32_t* idx, float* score, void* stream);
+
+/* rsm_forward_chunked with a router / decay variant: f is [B,T,Hh] or, with f_per_slot,
+ * [B,T,Hh,M]; noise, if given, is [B,T,Hh,M].  Same workspace size. */
+int rsm_forward_chunked_ex(const void* q, const void* k, const void* z, const void* v, int dtype,
+                           const float* f, const float* H0, int64_t B, int64_t T, int64_t Hh,
+                           int64_t M, int64_t Dv, int64_t K, int64_t C, float* o, float* H_out,
+                           int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                           const rsm_router_opts* opts, void* stream);
+
+/* rsm_decode_step with a router / decay variant: f is [B,Hh] or, with f_per_slot,
+ * [B,Hh,M]; noise, if given, is [B,Hh,M]. */
+int rsm_decode_step_ex(const void* q, const void* k, const void* z, const void* v, int dtype,
+                       const float* f, float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv,
+                       int64_t K, float* o, int32_t* idx_out, const rsm_router_opts* opts,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

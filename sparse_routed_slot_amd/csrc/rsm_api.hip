@@ -36,6 +36,18 @@ bool overlap(Range a, Range b) {
     return a0 < b0 + b.n && b0 < a0 + a.n;
 }
 
+// Validated kernel-side copy of a router variant (nullptr = the default router).
+bool router_opts(const rsm_router_opts* in, rsm::RouterOpts& out) {
+    out = rsm::RouterOpts{0, 0, 0, nullptr};
+    if (!in) return true;
+    if ((in->score != RSM_SCORE_SIGMOID && in->score != RSM_SCORE_SOFTMAX) || (in->normalize & ~1) ||
+        (in->f_per_slot & ~1))
+        return false;
+    if (reinterpret_cast<uintptr_t>(in->noise) % 16 != 0) return false;  // read as float4 rows
+    out = rsm::RouterOpts{in->score, in->normalize, in->f_per_slot, in->noise};
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,10 +67,17 @@ const char* rsm_status_string(int status) {
     return "unknown status";
 }
 
-int rsm_abi_version(void) { return 10000; }
+int rsm_abi_version(void) { return 10100; }
 
 int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t K,
                    int32_t* idx, float* score, void* stream) {
+    return rsm_route_topk_ex(z, dtype, nullptr, B, T, Hh, M, K, idx, score, stream);
+}
+
+int rsm_route_topk_ex(const void* z, int dtype, const rsm_router_opts* opts, int64_t B, int64_t T, int64_t Hh,
+                      int64_t M, int64_t K, int32_t* idx, float* score, void* stream) {
+    rsm::RouterOpts op;
+    if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
     if (B < 0 || T < 0 || Hh < 0 || !m_ok(M)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
@@ -67,9 +86,10 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
     if (rows == 0) return RSM_OK;
     if (!z || !idx) return RSM_ERR_NULL;
     const Range rz{z, size_t(rows * M) * esize(dtype)}, ri{idx, size_t(rows * K) * 4},
-        rs{score, size_t(rows * K) * 4};
-    if (overlap(ri, rz) || overlap(rs, rz) || overlap(ri, rs)) return RSM_ERR_ALIAS;
-    return rsm::route_topk_launch(z, dtype, long(rows), int(M), int(K), idx, score,
+        rs{score, size_t(rows * K) * 4}, rn{op.noise, size_t(rows * M) * 4};
+    if (overlap(ri, rz) || overlap(rs, rz) || overlap(ri, rs) || overlap(ri, rn) || overlap(rs, rn))
+        return RSM_ERR_ALIAS;
+    return rsm::route_topk_launch(z, dtype, long(rows), int(M), int(K), idx, score, op,
                                   static_cast<hipStream_t>(stream));
 }
 
@@ -85,6 +105,16 @@ int rsm_forward_chunked(const void* q, const void* k, const void* z, const void*
                         const float* H0, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t Dv, int64_t K,
                         int64_t C, float* o, float* H_out, int32_t* idx_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
+    return rsm_forward_chunked_ex(q, k, z, v, dtype, f, H0, B, T, Hh, M, Dv, K, C, o, H_out, idx_out, workspace,
+                                  workspace_bytes, nullptr, stream);
+}
+
+int rsm_forward_chunked_ex(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
+                           const float* H0, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t Dv, int64_t K,
+                           int64_t C, float* o, float* H_out, int32_t* idx_out, void* workspace,
+                           size_t workspace_bytes, const rsm_router_opts* opts, void* stream) {
+    rsm::RouterOpts op;
+    if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
     if (B < 0 || T < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv) || !c_ok(C)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
@@ -99,10 +129,10 @@ int rsm_forward_chunked(const void* q, const void* k, const void* z, const void*
     const size_t need = rsm_forward_workspace_bytes(dtype, B, T, Hh, M, Dv, C, K);
     if (need > 0 && (!workspace || workspace_bytes < need)) return RSM_ERR_WORKSPACE;
     const Range rq{q, size_t(rows * M) * es}, rk{k, size_t(rows * M) * es}, rz{z, size_t(rows * M) * es},
-        rv{v, size_t(rows * Dv) * es}, rf{f, size_t(rows) * 4}, rh0{H0, size_t(heads * M * Dv) * 4},
-        ro{o, size_t(rows * Dv) * 4}, rh{H_out, size_t(heads * M * Dv) * 4}, ri{idx_out, size_t(rows * K) * 4},
-        rw{workspace, need};
-    const Range ins[] = {rq, rk, rz, rv, rf, rh0};
+        rv{v, size_t(rows * Dv) * es}, rf{f, size_t(rows) * (op.f_per_slot ? size_t(M) : 1) * 4},
+        rh0{H0, size_t(heads * M * Dv) * 4}, ro{o, size_t(rows * Dv) * 4}, rh{H_out, size_t(heads * M * Dv) * 4},
+        ri{idx_out, size_t(rows * K) * 4}, rw{workspace, need}, rn{op.noise, size_t(rows * M) * 4};
+    const Range ins[] = {rq, rk, rz, rv, rf, rn, rh0};
     const Range outs[] = {ro, ri, rw};
     for (const Range& a : outs) {
         for (const Range& b : ins)
@@ -110,17 +140,25 @@ int rsm_forward_chunked(const void* q, const void* k, const void* z, const void*
         if (overlap(a, rh)) return RSM_ERR_ALIAS;
     }
     if (overlap(ro, ri) || overlap(ro, rw) || overlap(ri, rw)) return RSM_ERR_ALIAS;
-    for (int j = 0; j < 5; ++j)
+    for (int j = 0; j < 6; ++j)
         if (overlap(rh, ins[j])) return RSM_ERR_ALIAS;
     if (overlap(rh, rh0) && H_out != H0) return RSM_ERR_ALIAS;
     return rsm::forward_chunked_launch(q, k, z, v, dtype, f, H0, long(B), long(T), long(Hh), int(M), int(Dv),
-                                       int(K), int(C), o, H_out, idx_out, workspace,
+                                       int(K), int(C), o, H_out, idx_out, workspace, op,
                                        static_cast<hipStream_t>(stream));
 }
 
 int rsm_decode_step(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
                     float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv, int64_t K, float* o,
                     int32_t* idx_out, void* stream) {
+    return rsm_decode_step_ex(q, k, z, v, dtype, f, H, B, Hh, M, Dv, K, o, idx_out, nullptr, stream);
+}
+
+int rsm_decode_step_ex(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
+                       float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv, int64_t K, float* o,
+                       int32_t* idx_out, const rsm_router_opts* opts, void* stream) {
+    rsm::RouterOpts op;
+    if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
     if (B < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
@@ -130,13 +168,14 @@ int rsm_decode_step(const void* q, const void* k, const void* z, const void* v, 
     if (!q || !k || !z || !v || !f || !H || !o) return RSM_ERR_NULL;
     const size_t es = esize(dtype);
     const Range rq{q, size_t(heads * M) * es}, rk{k, size_t(heads * M) * es}, rz{z, size_t(heads * M) * es},
-        rv{v, size_t(heads * Dv) * es}, rf{f, size_t(heads) * 4}, rh{H, size_t(heads * M * Dv) * 4},
-        ro{o, size_t(heads * Dv) * 4}, ri{idx_out, size_t(heads * K) * 4};
-    const Range ins[] = {rq, rk, rz, rv, rf};
+        rv{v, size_t(heads * Dv) * es}, rf{f, size_t(heads) * (op.f_per_slot ? size_t(M) : 1) * 4},
+        rh{H, size_t(heads * M * Dv) * 4}, ro{o, size_t(heads * Dv) * 4}, ri{idx_out, size_t(heads * K) * 4},
+        rn{op.noise, size_t(heads * M) * 4};
+    const Range ins[] = {rq, rk, rz, rv, rf, rn};
     for (const Range& b : ins)
         if (overlap(rh, b) || overlap(ro, b) || overlap(ri, b)) return RSM_ERR_ALIAS;
     if (overlap(ro, rh) || overlap(ri, rh) || overlap(ro, ri)) return RSM_ERR_ALIAS;
-    return rsm::decode_step_launch(q, k, z, v, dtype, f, H, long(heads), int(M), int(Dv), int(K), o, idx_out,
+    return rsm::decode_step_launch(q, k, z, v, dtype, f, H, long(heads), int(M), int(Dv), int(K), o, idx_out, op,
                                    static_cast<hipStream_t>(stream));
 }
 

@@ -5,6 +5,9 @@
 // decayed by alpha = exp(s*f) and written with (1-alpha)*k_i*v; o = q . H is read after
 // the update; the README names "fused recurrent kernels for generation" for this case.
 //
+// Router variants (softmax scores, renormalised weights, per-slot decay rates, logit noise)
+// run in the same kernel (EX), the router wave doing the extra reductions.
+//
 // One workgroup (256 threads) per head.  The fp32 state H [M, Dv] is streamed once as
 // float4 rows (Dv/4 threads per row); the loads are issued before the router runs so
 // the HBM latency overlaps with the top-K.  Wave 0 routes the M logits (lane = slot) and
@@ -16,13 +19,27 @@
 
 namespace rsm {
 
-template <typename T, int M, int DV>
+// Sum and maximum over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+// EX: router variant (op): logits z + noise ranked as fp32 values (32-bit keys), softmax or
+// sigmoid scores, optional renormalisation over the selected slots, per-slot decay rates.
+template <typename T, int M, int DV, bool EX>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ z, const T* __restrict__ v,
     const float* __restrict__ f, float* __restrict__ H, int K, float* __restrict__ o,
-    int32_t* __restrict__ idx_out) {
+    int32_t* __restrict__ idx_out, RouterOpts op) {
     constexpr int SPL = M > kWave ? M / kWave : 1;
-    constexpr int NB = Elem<T>::kKeyBits;
+    constexpr int NB = EX ? 32 : Elem<T>::kKeyBits;
     constexpr int TPR = DV / 4;               // threads per state row, one float4 each
     constexpr int RPP = 256 / TPR;            // rows covered per pass of the workgroup
     constexpr int RPT = (M + RPP - 1) / RPP;  // rows held per thread
@@ -54,11 +71,42 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         for (int r = 0; r < SPL; ++r) {
             const int slot = r * kWave + lane;
             zv[r] = slot < M ? Elem<T>::load(zb, slot) : 0.0f;
+            if (EX && op.noise && slot < M) zv[r] += op.noise[bh * M + slot];
             key[r] = slot < M ? order_key<NB>(zv[r]) : 0u;
         }
         bool sel[SPL];
         wave_topk<SPL, NB>(key, K, sel);
-        const float ft = f[bh];
+        float sc[SPL];
+        if constexpr (EX) {
+            float zmax = -INFINITY, rden = 1.0f, tot = 0.0f;
+            if (op.softmax) {
+#pragma unroll
+                for (int r = 0; r < SPL; ++r)
+                    if (r * kWave + lane < M) zmax = fmaxf(zmax, zv[r]);
+                zmax = wave_max(zmax);
+                float den = 0.0f;
+#pragma unroll
+                for (int r = 0; r < SPL; ++r)
+                    if (r * kWave + lane < M) den += __expf(zv[r] - zmax);
+                rden = 1.0f / wave_sum(den);
+            }
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) {
+                sc[r] = sel[r] ? (op.softmax ? __expf(zv[r] - zmax) * rden : sigmoidf_dev(zv[r])) : 0.0f;
+                tot += sc[r];
+            }
+            if (op.normalize) {
+                tot = wave_sum(tot);
+                if (tot > 0.0f) {
+                    const float rt = 1.0f / tot;
+#pragma unroll
+                    for (int r = 0; r < SPL; ++r) sc[r] *= rt;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) sc[r] = sel[r] ? sigmoidf_dev(zv[r]) : 0.0f;
+        }
 #pragma unroll
         for (int r = 0; r < SPL; ++r) {
             const int slot = r * kWave + lane;
@@ -66,7 +114,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 float a = 1.0f, wk = 0.0f;
                 int upd = 0;
                 if (sel[r]) {
-                    const float s = sigmoidf_dev(zv[r]);
+                    const float s = sc[r];
+                    const float ft = (EX && op.f_per_slot) ? f[bh * M + slot] : f[bh];
                     if (s > 0.0f) a = __expf(s * ft);
                     if (a != 1.0f) {
                         upd = 1;
@@ -127,21 +176,27 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <typename T, int M, int DV>
 static int launch_decode_mdv(const T* q, const T* k, const T* z, const T* v, const float* f, float* H,
-                             long n_heads, int K, float* o, int32_t* idx_out, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<T, M, DV>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
-                       k, z, v, f, H, K, o, idx_out);
+                             long n_heads, int K, float* o, int32_t* idx_out, const RouterOpts& op,
+                             hipStream_t stream) {
+    if (op.is_default())
+        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, false>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
+                           k, z, v, f, H, K, o, idx_out, op);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, true>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
+                           k, z, v, f, H, K, o, idx_out, op);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
 template <typename T, int M>
 static int launch_decode_m(const T* q, const T* k, const T* z, const T* v, const float* f, float* H,
-                           long n_heads, int Dv, int K, float* o, int32_t* idx_out, hipStream_t s) {
+                           long n_heads, int Dv, int K, float* o, int32_t* idx_out, const RouterOpts& op,
+                           hipStream_t s) {
     switch (Dv) {
-        case 16: return launch_decode_mdv<T, M, 16>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
-        case 32: return launch_decode_mdv<T, M, 32>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
-        case 64: return launch_decode_mdv<T, M, 64>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
-        case 128: return launch_decode_mdv<T, M, 128>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
-        case 256: return launch_decode_mdv<T, M, 256>(q, k, z, v, f, H, n_heads, K, o, idx_out, s);
+        case 16: return launch_decode_mdv<T, M, 16>(q, k, z, v, f, H, n_heads, K, o, idx_out, op, s);
+        case 32: return launch_decode_mdv<T, M, 32>(q, k, z, v, f, H, n_heads, K, o, idx_out, op, s);
+        case 64: return launch_decode_mdv<T, M, 64>(q, k, z, v, f, H, n_heads, K, o, idx_out, op, s);
+        case 128: return launch_decode_mdv<T, M, 128>(q, k, z, v, f, H, n_heads, K, o, idx_out, op, s);
+        case 256: return launch_decode_mdv<T, M, 256>(q, k, z, v, f, H, n_heads, K, o, idx_out, op, s);
     }
     return RSM_ERR_UNSUPPORTED;
 }
@@ -149,24 +204,24 @@ static int launch_decode_m(const T* q, const T* k, const T* z, const T* v, const
 template <typename T>
 static int launch_decode(const void* q, const void* k, const void* z, const void* v, const float* f,
                          float* H, long n_heads, int M, int Dv, int K, float* o, int32_t* idx_out,
-                         hipStream_t s) {
+                         const RouterOpts& op, hipStream_t s) {
     const T *qq = static_cast<const T*>(q), *kk = static_cast<const T*>(k), *zz = static_cast<const T*>(z),
             *vv = static_cast<const T*>(v);
     switch (M) {
-        case 16: return launch_decode_m<T, 16>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
-        case 32: return launch_decode_m<T, 32>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
-        case 64: return launch_decode_m<T, 64>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
-        case 128: return launch_decode_m<T, 128>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, s);
+        case 16: return launch_decode_m<T, 16>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
+        case 32: return launch_decode_m<T, 32>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
+        case 64: return launch_decode_m<T, 64>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
+        case 128: return launch_decode_m<T, 128>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
     }
     return RSM_ERR_UNSUPPORTED;
 }
 
 int decode_step_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                        const float* f, float* H, long n_heads, int M, int Dv, int K, float* o,
-                       int32_t* idx_out, hipStream_t stream) {
+                       int32_t* idx_out, const RouterOpts& op, hipStream_t stream) {
     if (n_heads == 0) return RSM_OK;
-    if (dtype == RSM_F32) return launch_decode<float>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, stream);
-    return launch_decode<bf16_t>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, stream);
+    if (dtype == RSM_F32) return launch_decode<float>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, op, stream);
+    return launch_decode<bf16_t>(q, k, z, v, f, H, n_heads, M, Dv, K, o, idx_out, op, stream);
 }
 
 }  // namespace rsm

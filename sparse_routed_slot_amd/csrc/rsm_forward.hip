@@ -122,7 +122,7 @@ static int dispatch_m(int dtype, int M, int C, int DT, const ScanArgs& a) {
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M, int Dv, int K,
                            int C, float* o, float* H_out, int32_t* idx_out, void* workspace,
-                           hipStream_t stream) {
+                           const RouterOpts& op, hipStream_t stream) {
     const long BH = B * Hh;
     if (BH == 0) return RSM_OK;
     if (T == 0) {
@@ -138,7 +138,7 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
     const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),
                      reinterpret_cast<float*>(ws + L.de_off)};
     int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.chunk, idx_out, rmask, ralpha,
-                              stream);
+                              op, stream);
     if (st != RSM_OK) return st;
     const ScanArgs a{q, k, v, H0, B, T, Hh, Dv, K, sg, rmask, ralpha, o, H_out, stream};
     return dispatch_m(dtype, M, L.chunk, L.dt, a);

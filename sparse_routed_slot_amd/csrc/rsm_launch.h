@@ -10,12 +10,21 @@
 
 namespace rsm {
 
+// Router / decay variant as the kernels take it (validated copy of rsm_router_opts).
+struct RouterOpts {
+    int softmax;        // scores: 0 sigmoid, 1 softmax over all M logits
+    int normalize;      // selected scores divided by their sum
+    int f_per_slot;     // f [.., M] instead of [..]
+    const float* noise; // fp32 [.., M] added to z, or nullptr
+    bool is_default() const { return !softmax && !normalize && !f_per_slot && !noise; }
+};
+
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx,
-                      float* score, hipStream_t stream);
+                      float* score, const RouterOpts& op, hipStream_t stream);
 
 int decode_step_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                        const float* f, float* H, long n_heads, int M, int Dv, int K, float* o,
-                       int32_t* idx_out, hipStream_t stream);
+                       int32_t* idx_out, const RouterOpts& op, hipStream_t stream);
 
 // Workspace of the chunked forward: the route of every token-head in (batch*head, padded
 // token) order -- a selection bit mask (uint64 words) and the alphas of the selected slots
@@ -34,11 +43,12 @@ struct FwdLayout {
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream);
+                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
+                     hipStream_t stream);
 
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,
                            int Dv, int K, int C, float* o, float* H_out, int32_t* idx_out,
-                           void* workspace, hipStream_t stream);
+                           void* workspace, const RouterOpts& op, hipStream_t stream);
 
 }  // namespace rsm

@@ -335,15 +335,129 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
     }
 }
 
+// Router variant (softmax scores, renormalised weights, per-slot decay rates, logit noise;
+// the cases the pages name besides the default router).  Same outputs and row mapping as
+// route_rows_kernel.  The logits are ranked as fp32 values z (+ noise, one fp32 add), with
+// packed 64-bit keys (value, then inverted slot); every score is formed in registers by a
+// static loop over the row, so the selected slots never index the row with a lane-varying
+// subscript.
+template <typename T, int M, bool kFwd, bool SMALLK>
+__global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__ z, const float* __restrict__ f,
+                                                           long n_rows, long T_len, int Hh, long T_pad, int K, int C,
+                                                           int32_t* __restrict__ idx, float* __restrict__ score,
+                                                           unsigned long long* __restrict__ rmask,
+                                                           float* __restrict__ ralpha, RouterOpts op) {
+    const int lane = threadIdx.x;
+    long row, t = 0, bh = 0;
+    if (kFwd) {
+        const long nbt = (T_len + 63) / 64;
+        bh = long(blockIdx.x) / nbt;
+        t = (long(blockIdx.x) % nbt) * 64 + lane;
+        if (t >= T_len) return;  // no cross-lane operations below
+        row = ((bh / Hh) * T_len + t) * Hh + bh % Hh;
+    } else {
+        row = long(blockIdx.x) * 64 + lane;
+        if (row >= n_rows) return;
+    }
+
+    RowRegs<T, M> x;
+    x.load(z + row * M);
+    float v[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = x.val(i);
+    if (op.noise) {
+        const float4* g4 = reinterpret_cast<const float4*>(op.noise + row * M);
+#pragma unroll
+        for (int c = 0; c < M / 4; ++c) {
+            const float4 g = g4[c];
+            v[4 * c] += g.x;
+            v[4 * c + 1] += g.y;
+            v[4 * c + 2] += g.z;
+            v[4 * c + 3] += g.w;
+        }
+    }
+    bool sel[M];
+    if (K == M) {
+#pragma unroll
+        for (int i = 0; i < M; ++i) sel[i] = true;
+    } else {
+        typedef typename RowKey<float>::type U;
+        U th;
+        if constexpr (SMALLK) th = row_threshold16<float, M>(v, K);
+        else th = row_threshold<float, M>(v, K);
+#pragma unroll
+        for (int i = 0; i < M; ++i) sel[i] = RowKey<float>::make(v[i], i) >= th;
+    }
+    // scores of every slot (0 where unselected), then the optional renormalisation
+    float zmax = v[0], rden = 1.0f;
+    if (op.softmax) {
+#pragma unroll
+        for (int i = 1; i < M; ++i) zmax = fmaxf(zmax, v[i]);
+        float den = 0.0f;
+#pragma unroll
+        for (int i = 0; i < M; ++i) den += __expf(v[i] - zmax);
+        rden = 1.0f / den;
+    }
+    float sc[M], tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        sc[i] = sel[i] ? (op.softmax ? __expf(v[i] - zmax) * rden : sigmoidf_dev(v[i])) : 0.0f;
+        tot += sc[i];
+    }
+    if (op.normalize && tot > 0.0f) {
+        const float rt = 1.0f / tot;
+#pragma unroll
+        for (int i = 0; i < M; ++i) sc[i] *= rt;
+    }
+
+    constexpr int MW = (M + 63) / 64;
+    const long dst = row * K;
+    if (kFwd) {
+        const long orow = bh * T_pad + t;
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) {
+            unsigned long long mk = 0ull;
+#pragma unroll
+            for (int i = 64 * wd; i < M && i < 64 * wd + 64; ++i) mk |= sel[i] ? 1ull << (i & 63) : 0ull;
+            rmask[orow * MW + wd] = mk;
+        }
+    }
+    float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
+    const float* frow = kFwd ? (op.f_per_slot ? f + row * M : f + row) : nullptr;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (sel[i]) {
+            if (kFwd) {
+                const float fi = frow[op.f_per_slot ? i : 0];
+                alist[long(n) * C] = sc[i] > 0.0f ? __expf(sc[i] * fi) : 1.0f;
+                if (idx) idx[dst + n] = i;
+            } else {
+                idx[dst + n] = i;
+                if (score) score[dst + n] = sc[i];
+            }
+            ++n;
+        }
+    }
+}
+
 template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K, int C,
-                       int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
+                       int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
+                       hipStream_t stream) {
     if (n_rows == 0) return RSM_OK;
     const long nblk = kFwd ? (n_rows / T_len) * ((T_len + 63) / 64) : (n_rows + 63) / 64;
     const dim3 grid(static_cast<unsigned>(nblk)), block(64);
     const size_t lds = 0;
+    const bool ex = !op.is_default();
 #define RSM_ROUTE_LAUNCH(MM)                                                                                   \
-    if (K <= 16 && MM >= 16)                                                                                      \
+    if (ex && K <= 16)                                                                                            \
+        hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows,    \
+                           T_len, Hh, T_pad, K, C, idx, score, rmask, ralpha, op);                                \
+    else if (ex)                                                                                                  \
+        hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, false>), grid, block, lds, stream, z, f, n_rows,   \
+                           T_len, Hh, T_pad, K, C, idx, score, rmask, ralpha, op);                                \
+    else if (K <= 16 && MM >= 16)                                                                                 \
         hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, \
                            T_pad, K, C, idx, score, rmask, ralpha);                                               \
     else                                                                                                          \
@@ -361,22 +475,23 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
 }
 
 int route_topk_launch(const void* z, int dtype, long n_rows, int M, int K, int32_t* idx, float* score,
-                      hipStream_t stream) {
+                      const RouterOpts& op, hipStream_t stream) {
     if (dtype == RSM_F32)
         return launch_rows<float, false>(static_cast<const float*>(z), nullptr, n_rows, 1, 1, 1, M, K, 1, idx, score,
-                                         nullptr, nullptr, stream);
+                                         nullptr, nullptr, op, stream);
     return launch_rows<bf16_t, false>(static_cast<const bf16_t*>(z), nullptr, n_rows, 1, 1, 1, M, K, 1, idx, score,
-                                      nullptr, nullptr, stream);
+                                      nullptr, nullptr, op, stream);
 }
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
-                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, hipStream_t stream) {
+                     int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
+                     hipStream_t stream) {
     const long n_rows = B * T * Hh;
     if (dtype == RSM_F32)
         return launch_rows<float, true>(static_cast<const float*>(z), f, n_rows, T, int(Hh), T_pad, M, K, C, idx_out,
-                                        nullptr, rmask, ralpha, stream);
+                                        nullptr, rmask, ralpha, op, stream);
     return launch_rows<bf16_t, true>(static_cast<const bf16_t*>(z), f, n_rows, T, int(Hh), T_pad, M, K, C, idx_out,
-                                     nullptr, rmask, ralpha, stream);
+                                     nullptr, rmask, ralpha, op, stream);
 }
 
 }  // namespace rsm

@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "bf16_bits", "bf16_to_f32", "make_inputs",
-    "make_workload", "decode_step_inputs", "as_f64",
+    "make_workload", "decode_step_inputs", "as_f64", "variant_inputs",
 ]
 
 
@@ -175,3 +175,19 @@ def decode_step_inputs(rng: np.random.Generator, B: int, Hh: int, M: int, Dv: in
     f = (-_softplus64(u)).astype(np.float32)
     enc = bf16_bits if dtype == "bf16" else (lambda a: np.ascontiguousarray(a, np.float32))
     return {"q": enc(q), "k": enc(k), "z": enc(z), "v": enc(v), "f": f}
+
+
+# ----------------------------------------------------------------------------------
+# Extra inputs of the router / decay variants
+# ----------------------------------------------------------------------------------
+def variant_inputs(rng: np.random.Generator, zshape) -> dict:
+    """Per-slot log-decay rates and router exploration noise for logits of shape zshape
+    (..., M), both fp32: f_slot = -softplus(u) with u ~ N(0, 1) (the scalar recipe drawn
+    per slot), noise = standard Gumbel draws -log(-log(U)), U ~ Uniform(0, 1) (the
+    exploration noise the caller adds during training).  Draw order: u, then U."""
+    u = rng.standard_normal(zshape, dtype=np.float32)
+    f_slot = (-_softplus64(u)).astype(np.float32)
+    U = rng.random(zshape, dtype=np.float64)
+    U = np.clip(U, 1e-12, 1.0 - 1e-12)
+    noise = (-np.log(-np.log(U))).astype(np.float32)
+    return {"f_slot": f_slot, "noise": noise}

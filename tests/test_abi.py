@@ -125,3 +125,43 @@ def test_decode_argument_errors(lib):
     assert dec(lib, H=None) == NULL
     assert dec(lib, o=F_) == ALIAS                     # o on top of H
     assert dec(lib, Hh=0) == OK
+
+
+class RouterOpts(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int), ("normalize", ctypes.c_int), ("f_per_slot", ctypes.c_int),
+                ("noise", P)]
+
+
+def test_variant_argument_errors(lib):
+    """Router variants: fields outside {0, 1}, a misaligned noise buffer and noise that
+    overlaps an output are refused before any launch; a NULL struct is the default router."""
+    O = ctypes.POINTER(RouterOpts)
+    lib.rsm_route_topk_ex.argtypes = [P, ctypes.c_int, O, I64, I64, I64, I64, I64, P, P, P]
+    lib.rsm_forward_chunked_ex.argtypes = [P, P, P, P, ctypes.c_int, P, P, I64, I64, I64, I64, I64, I64, I64,
+                                           P, P, P, P, ctypes.c_size_t, O, P]
+    lib.rsm_decode_step_ex.argtypes = [P, P, P, P, ctypes.c_int, P, P, I64, I64, I64, I64, I64, P, P, O, P]
+
+    def r(opts, idx=B_):
+        return lib.rsm_route_topk_ex(A, 1, opts, 1, 4, 2, 64, 4, idx, None, None)
+
+    def fw(opts, o=F_):
+        return lib.rsm_forward_chunked_ex(A, B_, C_, D_, 1, E_, None, 1, 100, 2, 64, 128, 8, 64, o, None, None,
+                                          P(0x900000), 1 << 30, opts, None)
+
+    def de(opts, o=G_):
+        return lib.rsm_decode_step_ex(A, B_, C_, D_, 1, E_, F_, 4, 2, 64, 128, 8, o, None, opts, None)
+
+    for bad in (RouterOpts(2, 0, 0, None), RouterOpts(0, 2, 0, None), RouterOpts(0, 0, -1, None),
+                RouterOpts(1, 0, 0, P(0x800004))):
+        assert r(ctypes.byref(bad)) == UNSUP
+        assert fw(ctypes.byref(bad)) == UNSUP
+        assert de(ctypes.byref(bad)) == UNSUP
+    ok = RouterOpts(1, 1, 1, P(0x800000))
+    assert r(ctypes.byref(ok), idx=P(0x800000)) == ALIAS          # idx on top of the noise
+    assert fw(ctypes.byref(ok), o=P(0x800000)) == ALIAS           # o on top of the noise
+    assert de(ctypes.byref(ok), o=P(0x800000)) == ALIAS
+    # per-slot f is M times longer: o right after a per-token f overlaps a per-slot one
+    per_slot = RouterOpts(0, 0, 1, None)
+    assert fw(ctypes.byref(per_slot), o=P(0x50000 + 100 * 2 * 4)) == ALIAS
+    assert lib.rsm_route_topk_ex(A, 1, None, 0, 4, 2, 64, 4, B_, None, None) == OK
+    assert lib.rsm_abi_version() == 10100

@@ -306,3 +306,93 @@ def test_decode_workload_prefill_and_steps(rsm):
         check_close(od.cpu().numpy()[samp], o_e2e, sc, TOL["bf16"], f"decode e2e step {step}")
         check_close(od.cpu().numpy()[samp], o_dec, sc, TOL["bf16"], f"decode-only step {step}")
         Hgpu_from = H.cpu().numpy()[samp].astype(np.float64)
+
+
+# ------------------------------------------------------------ router and decay variants
+VARIANTS = [  # score, normalize, per-slot f, noise
+    ("softmax", False, False, False),
+    ("sigmoid", True, False, False),
+    ("sigmoid", False, True, False),
+    ("sigmoid", False, False, True),
+    ("softmax", True, True, True),
+]
+VAR_SHAPES = [  # dtype, B, T, Hh, M, Dv, K, C
+    ("bf16", 2, 200, 3, 64, 128, 16, 64),
+    ("f32", 1, 130, 2, 32, 32, 8, 32),
+    ("bf16", 1, 90, 2, 128, 64, 24, 32),
+    ("bf16", 2, 77, 2, 16, 16, 16, 16),
+]
+
+
+def _vid(v):
+    return "-".join(str(x) for x in v)
+
+
+@pytest.mark.parametrize("shape", VAR_SHAPES, ids=_vid)
+@pytest.mark.parametrize("var", VARIANTS, ids=_vid)
+def test_variant_route_and_forward(rsm, var, shape):
+    score, normalize, per_slot, noisy = var
+    dtype, B, T, Hh, M, Dv, K, C = shape
+    log(f"variant {var} forward {shape}")
+    seed = zlib.crc32(repr((var, shape)).encode()) % 1000
+    d = gen.make_inputs(B, T, Hh, M, Dv, dtype, seed=seed, h0=True)
+    ex = gen.variant_inputs(np.random.default_rng(seed + 1), d["z"].shape)
+    noise = ex["noise"] if noisy else None
+    t = dev_inputs(d, "cuda")
+    f = torch.from_numpy(ex["f_slot"]).cuda() if per_slot else t["f"]
+    nz = torch.from_numpy(noise).cuda() if noisy else None
+    # router alone: indices bit-exact, weights to fp32 rounding
+    idx, sc = rsm.route_topk(t["z"], K, score=score, normalize=normalize, noise=nz)
+    torch.cuda.synchronize()
+    zr = gen.as_f64(d["z"], dtype)
+    nr = None if noise is None else noise.astype(np.float64)
+    ridx, rsc = oracle.route_topk(zr, K, noise=nr, score=score, normalize=normalize)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(sc.cpu().numpy(), rsc, rtol=2e-5, atol=1e-7)
+    # forward
+    poison_pool()
+    out = torch.full((B, T, Hh, Dv), float("nan"), device="cuda")
+    o, H, gidx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], f, K, C=C, H0=t["H0"], want_idx=True,
+                                     out=out, score=score, normalize=normalize, noise=nz)
+    torch.cuda.synchronize()
+    r = f64_inputs(d)
+    fr = ex["f_slot"].astype(np.float64) if per_slot else r["f"]
+    ro, rH, ri = oracle.forward(r["q"], r["k"], r["z"], r["v"], fr, K, H0=r["H0"], noise=nr, score=score,
+                                normalize=normalize)
+    assert np.array_equal(gidx.cpu().numpy(), ri)
+    scale = float(np.max(np.abs(ro)))
+    eo = check_close(o.cpu().numpy(), ro, scale, TOL[dtype], f"variant {var} o")
+    check_close(H.cpu().numpy(), rH, scale, TOL[dtype], f"variant {var} H")
+    log(f"  err_o {eo / scale:.2e} rel")
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=_vid)
+@pytest.mark.parametrize("case", [("bf16", 3, 4, 64, 128, 16), ("f32", 2, 2, 128, 64, 40), ("bf16", 4, 2, 16, 32, 3)],
+                         ids=_vid)
+def test_variant_decode(rsm, var, case):
+    score, normalize, per_slot, noisy = var
+    dtype, B, Hh, M, Dv, K = case
+    log(f"variant {var} decode {case}")
+    rng = np.random.default_rng(zlib.crc32(repr((var, case)).encode()) % 1000)
+    H = torch.from_numpy(rng.standard_normal((B, Hh, M, Dv), dtype=np.float32)).cuda()
+    for step in range(6):
+        s = gen.decode_step_inputs(rng, B, Hh, M, Dv, dtype)
+        ex = gen.variant_inputs(rng, (B, Hh, M))
+        f = ex["f_slot"] if per_slot else s["f"]
+        if step == 3:
+            f = np.full_like(f, -np.inf)
+        noise = ex["noise"] if noisy else None
+        Hprev = H.clone()
+        t = {n: to_torch(s[n], dtype, "cuda") for n in "qkzv"}
+        o, idx = rsm.decode_step(t["q"], t["k"], t["z"], t["v"], torch.from_numpy(np.ascontiguousarray(f)).cuda(),
+                                 H, K, want_idx=True, score=score, normalize=normalize,
+                                 noise=None if noise is None else torch.from_numpy(noise).cuda())
+        torch.cuda.synchronize()
+        Hr = Hprev.cpu().numpy().astype(np.float64)
+        ro, ridx = oracle.decode_step(*(gen.as_f64(s[n], dtype) for n in "qkzv"), f.astype(np.float64), Hr, K,
+                                      noise=None if noise is None else noise.astype(np.float64), score=score,
+                                      normalize=normalize)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        scale = float(np.max(np.abs(ro)))
+        check_close(o.cpu().numpy(), ro, scale, TOL[dtype], f"variant decode o step {step}")
+        check_close(H.cpu().numpy(), Hr, scale, TOL[dtype], f"variant decode H step {step}")
