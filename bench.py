@@ -5,7 +5,9 @@ chunk contractions, state scan and emit) over one batch of the 400M-scale layer 
 Dv=128, top-16, C=64, bf16 q/k/z/v, fp32 f/state/outputs.  Three input sets are rotated
 so the ~154 MB working set cannot sit in the 256 MB last-level cache between steps.
 The decode step (256 sequences x 16 heads, M64 Dv128 K16, prefill T=512) is timed in the
-same run: 1024 back-to-back rsm_decode_step calls between two HIP events.
+same run: 1024 back-to-back rsm_decode_step calls between two HIP events.  So are the
+router / decay variants (softmax scores renormalised over the selected slots and one decay
+rate per slot; with and without exploration noise on the logits) on both workloads.
 
 Prints one JSON line.  Inputs are synthetic (seeded generator), already resident in HBM
 when the timed region starts.  The benchmark runs on one GPU: `--gpus N` with N > 1 is refused.
@@ -43,6 +45,12 @@ def decode_bytes(B, Hh, M, Dv, K, es):
     """Per step: full state read, K rows written back, inputs read, o written."""
     return (B * Hh * M * Dv * 4 + B * Hh * K * Dv * 4 + 3 * B * Hh * M * es + B * Hh * Dv * es
             + B * Hh * 4 + B * Hh * Dv * 4)
+
+
+def variant_extra_bytes(rows, M):
+    """Extra input bytes of the decode variant timed here: per-slot decay rates in place of
+    one per token-head, and the fp32 noise on the logits."""
+    return rows * (M - 1) * 4 + rows * M * 4
 
 
 def forward_sources_sha256():
@@ -156,6 +164,35 @@ def main():
     print(f"[bench] forward: wall {ms_per_step * 1e3:.1f} us/step, events {kernel_ms * 1e3:.1f} us "
           f"(min {min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # router / decay variants on the same workload (softmax + renormalised + per-slot f + noise)
+    vx = [gen.variant_inputs(np.random.default_rng(w.seed + 7 + i), host_sets[i]["z"].shape) for i in range(3)]
+    vdev = [{"f": torch.from_numpy(x["f_slot"]).cuda(), "noise": torch.from_numpy(x["noise"]).cuda()} for x in vx]
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    var_fwd = {}
+    for label, noisy in (("forward_inference", False), ("forward_training_noise", True)):
+        def fwd_var(i):
+            s, x = sets[i % len(sets)], vdev[i % len(vdev)]
+            rsm.forward_chunked(s["q"], s["k"], s["z"], s["v"], x["f"], w.K, C=w.C, workspace=ws, out=o,
+                                state_out=Hs, score="softmax", normalize=True, noise=x["noise"] if noisy else None)
+
+        for i in range(3):
+            fwd_var(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fwd_var(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        var_ms = e0.elapsed_time(e1) / args.steps
+        var_bytes = fbytes + w.B * w.T * w.Hh * (w.M - 1) * 4 + (w.B * w.T * w.Hh * w.M * 4 if noisy else 0)
+        print(f"[bench] {label} (router/decay variant): {var_ms * 1e3:.1f} us, "
+              f"{var_bytes / (var_ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+        var_fwd[label] = {"us_per_call": var_ms * 1e3, "algorithmic_bytes_per_launch": var_bytes,
+                          "achieved": var_bytes / (var_ms * 1e-3) / 1e9, "unit": "GB/s",
+                          "frac": var_bytes / (var_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del vdev
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -194,6 +231,28 @@ def main():
     print(f"[bench] decode: {dec_us:.2f} us/step, {dbytes / (dec_us * 1e-6) / 1e9:.0f} GB/s",
           file=sys.stderr, flush=True)
 
+    # decode with the router / decay variant
+    vpool = [{n: torch.from_numpy(x).cuda() for n, x in gen.variant_inputs(rng, (wd.B, wd.Hh, wd.M)).items()}
+             for _ in range(16)]
+
+    def dec_var(i):
+        s, x = pool[i % len(pool)], vpool[i % len(vpool)]
+        rsm.decode_step(s["q"], s["k"], s["z"], s["v"], x["f_slot"], Hdec, wd.K, out=od, score="softmax",
+                        normalize=True, noise=x["noise"])
+
+    for i in range(16):
+        dec_var(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.decode_steps):
+        dec_var(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dvar_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    dvar_bytes = dbytes + variant_extra_bytes(wd.B * wd.Hh, wd.M)
+    print(f"[bench] decode, router/decay variant: {dvar_us:.2f} us/step, "
+          f"{dvar_bytes / (dvar_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+
     rec = {
         "metric": METRIC,
         "value": tok / (ms_per_step * 1e-3),
@@ -221,6 +280,14 @@ def main():
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                             "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes},
+        "variants": {
+            "router": "softmax scores renormalised over the selected slots and per-slot decay rates; "
+                      "the training line and the decode add fp32 exploration noise on the logits",
+            **var_fwd,
+            "decode": {"us_per_step": dvar_us, "algorithmic_bytes_per_launch": dvar_bytes,
+                       "achieved": dvar_bytes / (dvar_us * 1e-6) / 1e9, "unit": "GB/s",
+                       "frac": dvar_bytes / (dvar_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        },
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)

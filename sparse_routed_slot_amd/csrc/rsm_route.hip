@@ -337,16 +337,19 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 
 // Router variant (softmax scores, renormalised weights, per-slot decay rates, logit noise;
 // the cases the pages name besides the default router).  Same outputs and row mapping as
-// route_rows_kernel.  The logits are ranked as fp32 values z (+ noise, one fp32 add), with
-// packed 64-bit keys (value, then inverted slot); every score is formed in registers by a
-// static loop over the row, so the selected slots never index the row with a lane-varying
-// subscript.
-template <typename T, int M, bool kFwd, bool SMALLK>
+// route_rows_kernel.  Without noise the selection is that of the default router (the
+// scores are increasing in the logits), so it uses the same top-K; with noise the logits
+// z + g (one fp32 add) are ranked with packed 64-bit keys (value, then inverted slot).
+// The selected slots are walked in ascending order as in route_rows_kernel, their logits
+// (and noise) read again from the rows just loaded; the softmax denominator is a sum over
+// the whole row.
+template <typename T, int M, bool kFwd, bool SMALLK, bool NOISY>
 __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__ z, const float* __restrict__ f,
                                                            long n_rows, long T_len, int Hh, long T_pad, int K, int C,
                                                            int32_t* __restrict__ idx, float* __restrict__ score,
                                                            unsigned long long* __restrict__ rmask,
                                                            float* __restrict__ ralpha, RouterOpts op) {
+    typedef typename RowKey<T>::type U;
     const int lane = threadIdx.x;
     long row, t = 0, bh = 0;
     if (kFwd) {
@@ -362,82 +365,123 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
 
     RowRegs<T, M> x;
     x.load(z + row * M);
-    float v[M];
+    const float* grow = NOISY ? op.noise + row * M : nullptr;
+    constexpr int MW = (M + 63) / 64;
+    unsigned long long mk[MW];
 #pragma unroll
-    for (int i = 0; i < M; ++i) v[i] = x.val(i);
-    if (op.noise) {
-        const float4* g4 = reinterpret_cast<const float4*>(op.noise + row * M);
+    for (int wd = 0; wd < MW; ++wd) mk[wd] = (M - 64 * wd >= 64) ? ~0ull : ((1ull << (M - 64 * wd)) - 1ull);
+    float zmax = 0.0f, rden = 1.0f;
+    {
+        float v[M];
 #pragma unroll
-        for (int c = 0; c < M / 4; ++c) {
-            const float4 g = g4[c];
-            v[4 * c] += g.x;
-            v[4 * c + 1] += g.y;
-            v[4 * c + 2] += g.z;
-            v[4 * c + 3] += g.w;
+        for (int i = 0; i < M; ++i) v[i] = x.val(i);
+        if constexpr (NOISY) {
+            const float4* g4 = reinterpret_cast<const float4*>(grow);
+#pragma unroll
+            for (int c = 0; c < M / 4; ++c) {
+                const float4 g = g4[c];
+                v[4 * c] += g.x;
+                v[4 * c + 1] += g.y;
+                v[4 * c + 2] += g.z;
+                v[4 * c + 3] += g.w;
+            }
+        }
+        if (K < M) {
+#pragma unroll
+            for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
+            constexpr bool kPacked = std::is_same<T, bf16_t>::value && M >= 32 && SMALLK;
+            if constexpr (kPacked && !NOISY) {
+                pk_select<M>(x.r, K, mk);
+            } else if constexpr (!NOISY) {
+                U th;
+                if constexpr (SMALLK) th = row_threshold16<T, M>(v, K);
+                else th = row_threshold<T, M>(v, K);
+#pragma unroll
+                for (int i = 0; i < M; ++i)
+                    if (RowKey<T>::make(v[i], i) >= th) mk[i >> 6] |= 1ull << (i & 63);
+            } else {
+                typename RowKey<float>::type th;
+                if constexpr (SMALLK) th = row_threshold16<float, M>(v, K);
+                else th = row_threshold<float, M>(v, K);
+#pragma unroll
+                for (int i = 0; i < M; ++i)
+                    if (RowKey<float>::make(v[i], i) >= th) mk[i >> 6] |= 1ull << (i & 63);
+            }
+        }
+        if (op.softmax) {
+            zmax = v[0];
+#pragma unroll
+            for (int i = 1; i < M; ++i) zmax = fmaxf(zmax, v[i]);
+            float den = 0.0f;
+#pragma unroll
+            for (int i = 0; i < M; ++i) den += __expf(v[i] - zmax);
+            rden = 1.0f / den;
         }
     }
-    bool sel[M];
-    if (K == M) {
-#pragma unroll
-        for (int i = 0; i < M; ++i) sel[i] = true;
-    } else {
-        typedef typename RowKey<float>::type U;
-        U th;
-        if constexpr (SMALLK) th = row_threshold16<float, M>(v, K);
-        else th = row_threshold<float, M>(v, K);
-#pragma unroll
-        for (int i = 0; i < M; ++i) sel[i] = RowKey<float>::make(v[i], i) >= th;
-    }
-    // scores of every slot (0 where unselected), then the optional renormalisation
-    float zmax = v[0], rden = 1.0f;
-    if (op.softmax) {
-#pragma unroll
-        for (int i = 1; i < M; ++i) zmax = fmaxf(zmax, v[i]);
-        float den = 0.0f;
-#pragma unroll
-        for (int i = 0; i < M; ++i) den += __expf(v[i] - zmax);
-        rden = 1.0f / den;
-    }
-    float sc[M], tot = 0.0f;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        sc[i] = sel[i] ? (op.softmax ? __expf(v[i] - zmax) * rden : sigmoidf_dev(v[i])) : 0.0f;
-        tot += sc[i];
-    }
-    if (op.normalize && tot > 0.0f) {
-        const float rt = 1.0f / tot;
-#pragma unroll
-        for (int i = 0; i < M; ++i) sc[i] *= rt;
-    }
-
-    constexpr int MW = (M + 63) / 64;
+    const T* zrow = z + row * M;
+    auto logit = [&](int i) { return NOISY ? Elem<T>::load(zrow, i) + grow[i] : Elem<T>::load(zrow, i); };
+    auto weight = [&](float zi) { return op.softmax ? __expf(zi - zmax) * rden : sigmoidf_dev(zi); };
     const long dst = row * K;
     if (kFwd) {
         const long orow = bh * T_pad + t;
 #pragma unroll
-        for (int wd = 0; wd < MW; ++wd) {
-            unsigned long long mk = 0ull;
-#pragma unroll
-            for (int i = 64 * wd; i < M && i < 64 * wd + 64; ++i) mk |= sel[i] ? 1ull << (i & 63) : 0ull;
-            rmask[orow * MW + wd] = mk;
-        }
+        for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
     }
     float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
     const float* frow = kFwd ? (op.f_per_slot ? f + row * M : f + row) : nullptr;
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        if (sel[i]) {
-            if (kFwd) {
-                const float fi = frow[op.f_per_slot ? i : 0];
-                alist[long(n) * C] = sc[i] > 0.0f ? __expf(sc[i] * fi) : 1.0f;
-                if (idx) idx[dst + n] = i;
-            } else {
-                idx[dst + n] = i;
-                if (score) score[dst + n] = sc[i];
-            }
-            ++n;
+    auto emit = [&](int n, int i, float s) {
+        if (kFwd) {
+            const float fi = frow[op.f_per_slot ? i : 0];
+            alist[long(n) * C] = s > 0.0f ? __expf(s * fi) : 1.0f;
+            if (idx) idx[dst + n] = i;
+        } else {
+            idx[dst + n] = i;
+            if (score) score[dst + n] = s;
         }
+    };
+    auto next_slot = [&](unsigned long long& m0, unsigned long long& m1) {
+        int i;
+        if (MW == 1 || m0 != 0ull) {
+            i = m0 != 0ull ? __builtin_ctzll(m0) : 0;
+            m0 &= m0 - 1ull;
+        } else {
+            i = 64 + __builtin_ctzll(m1);
+            m1 &= m1 - 1ull;
+        }
+        return i;
+    };
+    unsigned long long m0 = mk[0], m1 = MW > 1 ? mk[MW - 1] : 0ull;
+    if constexpr (SMALLK) {
+        int sl[16];
+        float sc[16], tot = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const int i = next_slot(m0, m1);
+            sl[n] = n < K ? i : 0;
+        }
+#pragma unroll
+        for (int n = 0; n < 16; ++n) sc[n] = logit(sl[n]);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            sc[n] = n < K ? weight(sc[n]) : 0.0f;
+            tot += sc[n];
+        }
+        const float rt = (op.normalize && tot > 0.0f) ? 1.0f / tot : 1.0f;
+#pragma unroll
+        for (int n = 0; n < 16; ++n)
+            if (n < K) emit(n, sl[n], sc[n] * rt);
+        return;
+    }
+    float rt = 1.0f;
+    if (op.normalize) {
+        unsigned long long a0 = m0, a1 = m1;
+        float tot = 0.0f;
+        for (int n = 0; n < K; ++n) tot += weight(logit(next_slot(a0, a1)));
+        if (tot > 0.0f) rt = 1.0f / tot;
+    }
+    for (int n = 0; n < K; ++n) {
+        const int i = next_slot(m0, m1);
+        emit(n, i, weight(logit(i)) * rt);
     }
 }
 
@@ -450,13 +494,18 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
     const dim3 grid(static_cast<unsigned>(nblk)), block(64);
     const size_t lds = 0;
     const bool ex = !op.is_default();
+#define RSM_ROUTE_EX(MM, SK, NZ)                                                                               \
+    hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, SK, NZ>), grid, block, lds, stream, z, f, n_rows, T_len,  \
+                       Hh, T_pad, K, C, idx, score, rmask, ralpha, op)
 #define RSM_ROUTE_LAUNCH(MM)                                                                                   \
-    if (ex && K <= 16)                                                                                            \
-        hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows,    \
-                           T_len, Hh, T_pad, K, C, idx, score, rmask, ralpha, op);                                \
+    if (ex && K <= 16 && op.noise)                                                                                \
+        RSM_ROUTE_EX(MM, true, true);                                                                             \
+    else if (ex && K <= 16)                                                                                       \
+        RSM_ROUTE_EX(MM, true, false);                                                                            \
+    else if (ex && op.noise)                                                                                      \
+        RSM_ROUTE_EX(MM, false, true);                                                                            \
     else if (ex)                                                                                                  \
-        hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, false>), grid, block, lds, stream, z, f, n_rows,   \
-                           T_len, Hh, T_pad, K, C, idx, score, rmask, ralpha, op);                                \
+        RSM_ROUTE_EX(MM, false, false);                                                                           \
     else if (K <= 16 && MM >= 16)                                                                                 \
         hipLaunchKernelGGL((route_rows_kernel<T, MM, kFwd, true>), grid, block, lds, stream, z, f, n_rows, T_len, Hh, \
                            T_pad, K, C, idx, score, rmask, ralpha);                                               \
@@ -471,6 +520,7 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
         default: return RSM_ERR_UNSUPPORTED;
     }
 #undef RSM_ROUTE_LAUNCH
+#undef RSM_ROUTE_EX
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
