@@ -677,16 +677,18 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     // chunk c into buffer NB.  E is an inclusive product scan across the lanes of the clamped
     // alphas.  Also the per-slot E at the chunk end and the flag of a product that left the
     // factored range.
-    // mid(): called once the route of chunk c has been read (the direct loads go there)
-    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW], auto&& mid)
+    // pre(): called first (direct loads into buffers prep does not read); mid(): called once
+    // the route of chunk c has been read (the direct loads go there)
+    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW], auto&& pre, auto&& mid)
                     __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
         E* sQK = NB ? sQK1 : sQK0;
         float al[SPW];
-        gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
         // q / k of this chunk are in: no later use of them has to wait behind the direct
         // loads issued next
         wait_vm<0>();
+        pre();
+        gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
         mid();
 #pragma unroll
         for (int j = 0; j < SPW; ++j) Ev[j] = clamp_alpha(al[j]);
@@ -937,8 +939,10 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         }
         // direct loads of v of chunk c+1 (its buffer was last read in the previous chunk) and
         // of the route of chunk c+2 (into the buffer chunk c's route was read from)
-        auto issue_next = [&]() {
+        auto issue_v_next = [&]() {
             if (c + 1 < c_end) issue_v(c + 1, NXT ? rv1 : rv0);
+        };
+        auto issue_route_next = [&]() {
             if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
         };
         float Ev[SPW];
@@ -967,7 +971,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         }
         // decay products and Qh / Kh of chunk c+1, then q / k of chunk c+2 into registers
         if constexpr (DP) {
-            prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev, issue_next);
+            prep(std::integral_constant<int, NXT>{}, c + 1, qc, kc, Ev, issue_v_next, issue_route_next);
             load_qk(c + 2, qn, kn);
             prep_tail(std::integral_constant<int, NXT>{}, Ev);
         }
@@ -1044,7 +1048,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             wg_barrier();  // the loads and the zero fill are done
             if constexpr (DP) {
                 float Ev[SPW];
-                prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev, [] {});
+                prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev, [] {}, [] {});
                 prep_tail(std::integral_constant<int, 0>{}, Ev);
             }
             wg_barrier();
