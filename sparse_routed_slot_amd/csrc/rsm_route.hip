@@ -244,6 +244,7 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 
     RowRegs<T, M> x;
     x.load(z + row * M);
+    const float ft = kFwd ? f[row] : 0.0f;  // issued with the row: its latency overlaps the top-K
     const bool all = (K == M);
     constexpr bool kPacked = std::is_same<T, bf16_t>::value && M >= 32 && SMALLK;
     U th = 0;
@@ -278,7 +279,6 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
         for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
     }
     float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
-    const float ft = kFwd ? f[row] : 0.0f;
     // walk the selected slots in ascending order (lowest set bit first); the logit of a
     // selected slot is read again from the row just loaded (cached)
     unsigned long long m0 = mk[0], m1 = MW > 1 ? mk[MW - 1] : 0ull;
