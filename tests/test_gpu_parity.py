@@ -396,3 +396,29 @@ def test_variant_decode(rsm, var, case):
         scale = float(np.max(np.abs(ro)))
         check_close(o.cpu().numpy(), ro, scale, TOL[dtype], f"variant decode o step {step}")
         check_close(H.cpu().numpy(), Hr, scale, TOL[dtype], f"variant decode H step {step}")
+
+
+@pytest.mark.parametrize("name", ["fwd_b8_t2048", "long_t32768"])
+@pytest.mark.parametrize("noisy", [False, True])
+def test_variant_forward_workloads(rsm, name, noisy):
+    """The benchmarked variant configurations at full size: softmax scores renormalised over
+    the selected slots with per-slot decay rates, with and without logit noise."""
+    log(f"variant forward workload {name} noise={noisy}")
+    d = gen.make_workload(name)
+    K, C, dtype = d["K"], d["C"], d["dtype"]
+    ex = gen.variant_inputs(np.random.default_rng(77), d["z"].shape)
+    t = dev_inputs(d, "cuda")
+    nz = torch.from_numpy(ex["noise"]).cuda() if noisy else None
+    poison_pool()
+    o, H, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], torch.from_numpy(ex["f_slot"]).cuda(), K, C=C,
+                                    H0=t["H0"], want_idx=True, score="softmax", normalize=True, noise=nz)
+    torch.cuda.synchronize()
+    r = f64_inputs(d)
+    ro, rH, ri = oracle.forward(r["q"], r["k"], r["z"], r["v"], ex["f_slot"].astype(np.float64), K, H0=r["H0"],
+                                noise=ex["noise"].astype(np.float64) if noisy else None, score="softmax",
+                                normalize=True)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    scale = float(np.max(np.abs(ro)))
+    eo = check_close(o.cpu().numpy(), ro, scale, TOL[dtype], f"{name} variant o")
+    check_close(H.cpu().numpy(), rH, scale, TOL[dtype], f"{name} variant H")
+    log(f"  err_o {eo / scale:.2e} rel")
