@@ -11,6 +11,8 @@ namespace {
 
 bool dtype_ok(int dtype) { return dtype == RSM_F32 || dtype == RSM_BF16; }
 bool m_ok(int64_t M) { return M == 16 || M == 32 || M == 64 || M == 128; }
+// the router and the decode step also take the pages' default slot count
+bool m_ok_rd(int64_t M) { return m_ok(M) || M == 256; }
 bool dv_ok(int64_t Dv) { return Dv == 16 || Dv == 32 || Dv == 64 || Dv == 128 || Dv == 256; }
 bool c_ok(int64_t C) { return C == 16 || C == 32 || C == 64; }
 size_t esize(int dtype) { return dtype == RSM_F32 ? 4 : 2; }
@@ -79,7 +81,7 @@ int rsm_route_topk_ex(const void* z, int dtype, const rsm_router_opts* opts, int
     rsm::RouterOpts op;
     if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
-    if (B < 0 || T < 0 || Hh < 0 || !m_ok(M)) return RSM_ERR_SHAPE;
+    if (B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
     const int64_t rows = mul_ck({B, T, Hh});
     if (rows < 0 || rows / 4 >= (int64_t(1) << 31)) return RSM_ERR_SHAPE;
@@ -160,10 +162,10 @@ int rsm_decode_step_ex(const void* q, const void* k, const void* z, const void* 
     rsm::RouterOpts op;
     if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
-    if (B < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv)) return RSM_ERR_SHAPE;
+    if (B < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
     const int64_t heads = mul_ck({B, Hh});
-    if (heads < 0 || heads >= (int64_t(1) << 31) || mul_ck({heads, M, Dv}) < 0) return RSM_ERR_SHAPE;
+    if (heads < 0 || heads >= (int64_t(1) << 29) || mul_ck({heads, M, Dv}) < 0) return RSM_ERR_SHAPE;
     if (heads == 0) return RSM_OK;
     if (!q || !k || !z || !v || !f || !H || !o) return RSM_ERR_NULL;
     const size_t es = esize(dtype);

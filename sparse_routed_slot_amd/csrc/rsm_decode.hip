@@ -19,20 +19,13 @@
 
 namespace rsm {
 
-// Sum and maximum over the 64 lanes of a wave (every lane gets the result).
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
-    return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
 // EX: router variant (op): logits z + noise ranked as fp32 values (32-bit keys), softmax or
 // sigmoid scores, optional renormalisation over the selected slots, per-slot decay rates.
+// DTC: state columns per workgroup (the whole row unless M * DV is large; then each column
+// tile's workgroup routes the token again, which is cheap, and only tile 0 writes idx_out).
+template <int M, int DV>
+constexpr int decode_cols() { return DV < 16384 / M ? DV : 16384 / M; }
+
 template <typename T, int M, int DV, bool EX>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ z, const T* __restrict__ v,
@@ -40,17 +33,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     int32_t* __restrict__ idx_out, RouterOpts op) {
     constexpr int SPL = M > kWave ? M / kWave : 1;
     constexpr int NB = EX ? 32 : Elem<T>::kKeyBits;
-    constexpr int TPR = DV / 4;               // threads per state row, one float4 each
+    constexpr int DTC = decode_cols<M, DV>(), NTL = DV / DTC;
+    constexpr int TPR = DTC / 4;              // threads per state row, one float4 each
     constexpr int RPP = 256 / TPR;            // rows covered per pass of the workgroup
     constexpr int RPT = (M + RPP - 1) / RPP;  // rows held per thread
     __shared__ float s_a[M], s_wk[M], s_q[M];
     __shared__ int s_upd[M];
     __shared__ float4 s_red[RPP][TPR];
 
-    const long bh = blockIdx.x;
+    const long bh = blockIdx.x / NTL;
+    const int tile = int(blockIdx.x % NTL), c0 = tile * DTC;
     const int tid = threadIdx.x;
     const int cg = tid % TPR, rg = tid / TPR;
-    float* Hb = H + bh * long(M) * DV;
+    float* Hb = H + bh * long(M) * DV + c0;
 
     float4 hv[RPT];
 #pragma unroll
@@ -58,7 +53,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const int row = rg + j * RPP;
         if (row < M) hv[j] = *reinterpret_cast<const float4*>(Hb + row * DV + 4 * cg);
     }
-    const T* vb = v + bh * DV + 4 * cg;
+    const T* vb = v + bh * DV + c0 + 4 * cg;
     const float4 vv = make_float4(Elem<T>::load(vb, 0), Elem<T>::load(vb, 1), Elem<T>::load(vb, 2),
                                   Elem<T>::load(vb, 3));
 
@@ -128,7 +123,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 s_q[slot] = Elem<T>::load(q + bh * M, slot);
             }
         }
-        if (idx_out) {
+        if (idx_out && tile == 0) {
             int pos[SPL];
             wave_compact<SPL>(sel, pos);
 #pragma unroll
@@ -170,7 +165,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             sum.z += p.z;
             sum.w += p.w;
         }
-        *reinterpret_cast<float4*>(o + bh * DV + 4 * cg) = sum;
+        *reinterpret_cast<float4*>(o + bh * DV + c0 + 4 * cg) = sum;
     }
 }
 
@@ -178,12 +173,13 @@ template <typename T, int M, int DV>
 static int launch_decode_mdv(const T* q, const T* k, const T* z, const T* v, const float* f, float* H,
                              long n_heads, int K, float* o, int32_t* idx_out, const RouterOpts& op,
                              hipStream_t stream) {
+    const dim3 grid(unsigned(n_heads * (DV / decode_cols<M, DV>())));
     if (op.is_default())
-        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, false>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
-                           k, z, v, f, H, K, o, idx_out, op);
+        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, false>), grid, dim3(256), 0, stream, q, k, z, v, f, H, K, o,
+                           idx_out, op);
     else
-        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, true>), dim3(unsigned(n_heads)), dim3(256), 0, stream, q,
-                           k, z, v, f, H, K, o, idx_out, op);
+        hipLaunchKernelGGL((decode_step_kernel<T, M, DV, true>), grid, dim3(256), 0, stream, q, k, z, v, f, H, K, o,
+                           idx_out, op);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
@@ -212,6 +208,7 @@ static int launch_decode(const void* q, const void* k, const void* z, const void
         case 32: return launch_decode_m<T, 32>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
         case 64: return launch_decode_m<T, 64>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
         case 128: return launch_decode_m<T, 128>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
+        case 256: return launch_decode_m<T, 256>(qq, kk, zz, vv, f, H, n_heads, Dv, K, o, idx_out, op, s);
     }
     return RSM_ERR_UNSUPPORTED;
 }

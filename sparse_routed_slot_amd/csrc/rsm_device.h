@@ -104,6 +104,18 @@ __device__ __forceinline__ void wave_compact(const bool (&sel)[SPL], int (&pos)[
 
 __device__ __forceinline__ float sigmoidf_dev(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// Sum and maximum over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
 // ------------------------------------------------------------------------------------
 // Lane-per-row exact top-K: one lane owns one row of M logits in registers.
 //

@@ -485,6 +485,68 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
     }
 }
 
+// Public router for wide rows (M = 256, the pages' default slot count): one wave per row,
+// lane l holding slots r*64 + l, the exact top-K by the wave-wide bitwise threshold search
+// (rsm_device.h), then the scores (sigmoid, or softmax over the row) of the selected slots,
+// renormalised over them if asked, and each selected slot's position in the ascending list.
+template <typename T, int M, bool EX>
+__global__ __launch_bounds__(256) void route_wave_kernel(const T* __restrict__ z, long n_rows, int K,
+                                                         int32_t* __restrict__ idx, float* __restrict__ score,
+                                                         RouterOpts op) {
+    constexpr int SPL = M / kWave;
+    constexpr int NB = EX ? 32 : Elem<T>::kKeyBits;
+    const int lane = threadIdx.x & 63;
+    const long row = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows) return;  // the whole wave
+    float zv[SPL];
+    uint32_t key[SPL];
+#pragma unroll
+    for (int r = 0; r < SPL; ++r) {
+        zv[r] = Elem<T>::load(z + row * M, r * kWave + lane);
+        if (EX && op.noise) zv[r] += op.noise[row * M + r * kWave + lane];
+        key[r] = order_key<NB>(zv[r]);
+    }
+    bool sel[SPL];
+    wave_topk<SPL, NB>(key, K, sel);
+    float sc[SPL];
+    if constexpr (EX) {
+        float zmax = -INFINITY, rden = 1.0f, tot = 0.0f;
+        if (op.softmax) {
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) zmax = fmaxf(zmax, zv[r]);
+            zmax = wave_max(zmax);
+            float den = 0.0f;
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) den += __expf(zv[r] - zmax);
+            rden = 1.0f / wave_sum(den);
+        }
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            sc[r] = sel[r] ? (op.softmax ? __expf(zv[r] - zmax) * rden : sigmoidf_dev(zv[r])) : 0.0f;
+            tot += sc[r];
+        }
+        if (op.normalize) {
+            tot = wave_sum(tot);
+            if (tot > 0.0f) {
+                const float rt = 1.0f / tot;
+#pragma unroll
+                for (int r = 0; r < SPL; ++r) sc[r] *= rt;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) sc[r] = sel[r] ? sigmoidf_dev(zv[r]) : 0.0f;
+    }
+    int pos[SPL];
+    wave_compact<SPL>(sel, pos);
+#pragma unroll
+    for (int r = 0; r < SPL; ++r)
+        if (sel[r]) {
+            idx[row * K + pos[r]] = r * kWave + lane;
+            if (score) score[row * K + pos[r]] = sc[r];
+        }
+}
+
 template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K, int C,
                        int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
@@ -494,6 +556,15 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
     const dim3 grid(static_cast<unsigned>(nblk)), block(64);
     const size_t lds = 0;
     const bool ex = !op.is_default();
+    if (M == 256) {  // public router only (the chunked forward takes M <= 128)
+        if (kFwd) return RSM_ERR_UNSUPPORTED;
+        const dim3 g4(static_cast<unsigned>((n_rows + 3) / 4)), b4(256);
+        if (ex)
+            hipLaunchKernelGGL((route_wave_kernel<T, 256, true>), g4, b4, 0, stream, z, n_rows, K, idx, score, op);
+        else
+            hipLaunchKernelGGL((route_wave_kernel<T, 256, false>), g4, b4, 0, stream, z, n_rows, K, idx, score, op);
+        return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
+    }
 #define RSM_ROUTE_EX(MM, SK, NZ)                                                                               \
     hipLaunchKernelGGL((route_rows_ex_kernel<T, MM, kFwd, SK, NZ>), grid, block, lds, stream, z, f, n_rows, T_len,  \
                        Hh, T_pad, K, C, idx, score, rmask, ralpha, op)

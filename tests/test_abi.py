@@ -120,6 +120,10 @@ def dec(lib, dtype=1, B=4, Hh=2, M=64, Dv=128, K=8, H=F_, o=G_, idx=None, q=A):
 def test_decode_argument_errors(lib):
     assert dec(lib, dtype=2) == DTYPE
     assert dec(lib, M=100) == SHAPE
+    assert dec(lib, M=512) == SHAPE
+    assert dec(lib, M=256, Hh=0) == OK                 # the router and decode take M = 256
+    assert route(lib, M=256, B=0) == OK and route(lib, M=512) == SHAPE
+    assert fwd(lib, M=256) == SHAPE                    # the chunked forward does not
     assert dec(lib, Dv=96) == SHAPE
     assert dec(lib, K=65) == KERR
     assert dec(lib, H=None) == NULL

@@ -80,7 +80,7 @@ def test_route_workloads(rsm, name):
     np.testing.assert_allclose(score.cpu().numpy(), rscore, rtol=2e-6, atol=1e-30)
 
 
-@pytest.mark.parametrize("M", [16, 32, 64, 128])
+@pytest.mark.parametrize("M", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_route_ties_and_signed_zeros(rsm, M, dtype):
     log(f"route ties M={M} {dtype}")
@@ -219,6 +219,9 @@ DEC = [
     ("f32", 2, 2, 128, 64, 8),
     ("bf16", 2, 2, 32, 256, 32),
     ("bf16", 5, 1, 128, 32, 128),
+    ("bf16", 3, 4, 128, 256, 16),
+    ("bf16", 2, 4, 256, 256, 32),   # the pages' default layer: 4 heads, 256 slots, top-32, head dim 256
+    ("f32", 2, 2, 256, 64, 16),
 ]
 
 
@@ -367,8 +370,8 @@ def test_variant_route_and_forward(rsm, var, shape):
 
 
 @pytest.mark.parametrize("var", VARIANTS, ids=_vid)
-@pytest.mark.parametrize("case", [("bf16", 3, 4, 64, 128, 16), ("f32", 2, 2, 128, 64, 40), ("bf16", 4, 2, 16, 32, 3)],
-                         ids=_vid)
+@pytest.mark.parametrize("case", [("bf16", 3, 4, 64, 128, 16), ("f32", 2, 2, 128, 64, 40), ("bf16", 4, 2, 16, 32, 3),
+                                  ("bf16", 2, 4, 256, 256, 32)], ids=_vid)
 def test_variant_decode(rsm, var, case):
     score, normalize, per_slot, noisy = var
     dtype, B, Hh, M, Dv, K = case
@@ -422,3 +425,23 @@ def test_variant_forward_workloads(rsm, name, noisy):
     eo = check_close(o.cpu().numpy(), ro, scale, TOL[dtype], f"{name} variant o")
     check_close(H.cpu().numpy(), rH, scale, TOL[dtype], f"{name} variant H")
     log(f"  err_o {eo / scale:.2e} rel")
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=_vid)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_variant_route_wide_rows(rsm, var, dtype):
+    """The router at the pages' default slot count (M = 256, K = 32), every variant."""
+    score, normalize, _, noisy = var
+    log(f"variant route M=256 {var} {dtype}")
+    rng = np.random.default_rng(zlib.crc32(repr((var, dtype)).encode()) % 1000)
+    z = (rng.standard_normal((2, 37, 4, 256), dtype=np.float32) * 1.5).astype(np.float32)
+    z[0, :3] = np.round(z[0, :3] * 2) / 2     # ties
+    enc = gen.bf16_bits(z) if dtype == "bf16" else z
+    noise = gen.variant_inputs(rng, z.shape)["noise"] if noisy else None
+    idx, sc = rsm.route_topk(to_torch(enc, dtype, "cuda"), 32, score=score, normalize=normalize,
+                             noise=None if noise is None else torch.from_numpy(noise).cuda())
+    torch.cuda.synchronize()
+    ridx, rsc = oracle.route_topk(gen.as_f64(enc, dtype), 32, noise=None if noise is None else noise.astype(np.float64),
+                                  score=score, normalize=normalize)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(sc.cpu().numpy(), rsc, rtol=2e-5, atol=1e-7)
