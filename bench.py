@@ -252,6 +252,31 @@ def main():
     dvar_bytes = dbytes + variant_extra_bytes(wd.B * wd.Hh, wd.M)
     print(f"[bench] decode, router/decay variant: {dvar_us:.2f} us/step, "
           f"{dvar_bytes / (dvar_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    del vpool, pool, Hdec
+
+    # decode step at the pages' default layer shape (4 heads, 256 slots, top-32, head dim 256),
+    # 256 sequences; the state is drawn at random (the chunked forward takes M <= 128)
+    LB, LHh, LM, LDv, LK = 256, 4, 256, 256, 32
+    Hl = torch.randn((LB, LHh, LM, LDv), dtype=torch.float32, device="cuda")
+    lpool = [to_dev(gen.decode_step_inputs(rng, LB, LHh, LM, LDv, "bf16"), torch) for _ in range(16)]
+    ol = torch.empty((LB, LHh, LDv), dtype=torch.float32, device="cuda")
+
+    def dec_layer(i):
+        s = lpool[i % len(lpool)]
+        rsm.decode_step(s["q"], s["k"], s["z"], s["v"], s["f"], Hl, LK, out=ol)
+
+    for i in range(16):
+        dec_layer(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.decode_steps):
+        dec_layer(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dl_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    dl_bytes = decode_bytes(LB, LHh, LM, LDv, LK, 2)
+    print(f"[bench] decode, default layer shape (B{LB} Hh{LHh} M{LM} Dv{LDv} K{LK}): {dl_us:.2f} us/step, "
+          f"{dl_bytes / (dl_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
     rec = {
         "metric": METRIC,
@@ -280,6 +305,11 @@ def main():
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                             "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes},
+        "decode_default_layer": {"config": {"B": LB, "Hh": LHh, "M": LM, "Dv": LDv, "K": LK,
+                                            "state": "random fp32", "step_input_pool": len(lpool)},
+                                 "us_per_step": dl_us, "algorithmic_bytes_per_launch": dl_bytes,
+                                 "achieved": dl_bytes / (dl_us * 1e-6) / 1e9, "unit": "GB/s",
+                                 "frac": dl_bytes / (dl_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
         "variants": {
             "router": "softmax scores renormalised over the selected slots and per-slot decay rates; "
                       "the training line and the decode add fp32 exploration noise on the logits",
