@@ -211,6 +211,7 @@ def main():
     del pre
     rng = np.random.default_rng(1000 + wd.seed)
     pool = [to_dev(gen.decode_step_inputs(rng, wd.B, wd.Hh, wd.M, wd.Dv, "bf16"), torch) for _ in range(16)]
+    n_pool = len(pool)
     od = torch.empty((wd.B, wd.Hh, wd.Dv), dtype=torch.float32, device="cuda")
 
     def dec(i):
@@ -259,6 +260,7 @@ def main():
     LB, LHh, LM, LDv, LK = 256, 4, 256, 256, 32
     Hl = torch.randn((LB, LHh, LM, LDv), dtype=torch.float32, device="cuda")
     lpool = [to_dev(gen.decode_step_inputs(rng, LB, LHh, LM, LDv, "bf16"), torch) for _ in range(16)]
+    n_lpool = len(lpool)
     ol = torch.empty((LB, LHh, LDv), dtype=torch.float32, device="cuda")
 
     def dec_layer(i):
@@ -295,7 +297,7 @@ def main():
                    "C": w.C, "inputs": "bf16 q,k,z,v; fp32 f, state, outputs", "input_sets_rotated": 3},
         "decode_us_per_step": dec_us,
         "decode_config": {"workload": wd.name, "B": wd.B, "Hh": wd.Hh, "M": wd.M, "Dv": wd.Dv, "K": wd.K,
-                          "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": len(pool)},
+                          "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": n_pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel pass A + "
@@ -306,7 +308,7 @@ def main():
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                             "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes},
         "decode_default_layer": {"config": {"B": LB, "Hh": LHh, "M": LM, "Dv": LDv, "K": LK,
-                                            "state": "random fp32", "step_input_pool": len(lpool)},
+                                            "state": "random fp32", "step_input_pool": n_lpool},
                                  "us_per_step": dl_us, "algorithmic_bytes_per_launch": dl_bytes,
                                  "achieved": dl_bytes / (dl_us * 1e-6) / 1e9, "unit": "GB/s",
                                  "frac": dl_bytes / (dl_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
