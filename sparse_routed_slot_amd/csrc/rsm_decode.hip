@@ -10,7 +10,7 @@
 //
 // One workgroup (256 threads) per head.  The fp32 state H [M, Dv] is streamed once as
 // float4 rows (Dv/4 threads per row); the loads are issued before the router runs so
-// the HBM latency overlaps with the top-K.  Wave 0 routes the M logits (lane = slot) and
+// the HBM latency overlaps with the top-K (the router's own inputs are issued first).  Wave 0 routes the M logits (lane = slot) and
 // publishes alpha, (1-alpha)*k and q per slot in LDS.  Every thread then updates the
 // selected rows it holds in registers, writes back only those rows, and accumulates its
 // partial read q_i*H[i,:]; a reduction over row groups in LDS finishes o.
@@ -47,6 +47,23 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int cg = tid % TPR, rg = tid / TPR;
     float* Hb = H + bh * long(M) * DV + c0;
 
+    // The router wave's inputs (z, q, k of every slot, noise, f) are loaded ahead of the
+    // state rows: they do not queue behind them, and no second round trip follows the top-K.
+    float zv[SPL], qv[SPL], kv[SPL], nv[SPL];
+    float ft0 = 0.0f;
+    if (tid < kWave) {
+        const long hb = bh * M;
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            const int slot = r * kWave + tid;
+            zv[r] = slot < M ? Elem<T>::load(z + hb, slot) : 0.0f;
+            qv[r] = slot < M ? Elem<T>::load(q + hb, slot) : 0.0f;
+            kv[r] = slot < M ? Elem<T>::load(k + hb, slot) : 0.0f;
+            nv[r] = (EX && op.noise && slot < M) ? op.noise[hb + slot] : 0.0f;
+        }
+        if (!(EX && op.f_per_slot)) ft0 = f[bh];
+    }
+
     float4 hv[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
@@ -59,14 +76,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     if (tid < kWave) {
         const int lane = tid;
-        const T* zb = z + bh * M;
         uint32_t key[SPL];
-        float zv[SPL];
 #pragma unroll
         for (int r = 0; r < SPL; ++r) {
             const int slot = r * kWave + lane;
-            zv[r] = slot < M ? Elem<T>::load(zb, slot) : 0.0f;
-            if (EX && op.noise && slot < M) zv[r] += op.noise[bh * M + slot];
+            if (EX && op.noise) zv[r] += nv[r];
             key[r] = slot < M ? order_key<NB>(zv[r]) : 0u;
         }
         bool sel[SPL];
@@ -110,17 +124,17 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
                 int upd = 0;
                 if (sel[r]) {
                     const float s = sc[r];
-                    const float ft = (EX && op.f_per_slot) ? f[bh * M + slot] : f[bh];
+                    const float ft = (EX && op.f_per_slot) ? f[bh * M + slot] : ft0;
                     if (s > 0.0f) a = __expf(s * ft);
                     if (a != 1.0f) {
                         upd = 1;
-                        wk = (1.0f - a) * Elem<T>::load(k + bh * M, slot);
+                        wk = (1.0f - a) * kv[r];
                     }
                 }
                 s_a[slot] = a;
                 s_wk[slot] = wk;
                 s_upd[slot] = upd;
-                s_q[slot] = Elem<T>::load(q + bh * M, slot);
+                s_q[slot] = qv[r];
             }
         }
         if (idx_out && tile == 0) {
