@@ -29,7 +29,7 @@
  *  - Errors: argument errors return a negative rsm_status before anything is enqueued;
  *    a failed launch returns RSM_ERR_HIP.  Data values are not validated: f > 0, NaN or
  *    infinite z/q/k/v give unspecified results.
- *  - Supported shapes: M in {16, 32, 64, 128}; Dv in {16, 32, 64, 128, 256};
+ *  - Supported shapes: M in {16, 32, 64, 128, 256}; Dv in {16, 32, 64, 128, 256};
  *    1 <= K <= M; chunk C in {16, 32, 64}; B, T, Hh >= 0 (T need not be a multiple of C;
  *    an empty call enqueues nothing except copying H0, or zeros, into H_out).
  */
@@ -80,7 +80,9 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
  * The workspace holds the route of every token-head, padded to whole chunks (a selection
  * bit mask, 8 bytes per 64 slots, and the K decay factors of the selected slots, fp32),
  * and, when few heads make the forward cut each sequence into S segments, the fp32 end
- * state (M x Dv) and decay product (M) of every segment but the last, per head.
+ * state (M x Dv) and decay product (M) of every segment but the last, per head.  With
+ * M = 256 it holds the router's output instead: K slot indices (int32) and K weights (fp32)
+ * per token-head.
  * Returns 0 for unsupported arguments as well; the forward call then reports the error.
  */
 size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
@@ -105,6 +107,10 @@ size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, 
  * a compute unit).
  * Chunks whose decay over the chunk falls below 2^-100 for some slot (f = -inf, or very
  * strong decay) are evaluated token by token instead of in factored form.
+ * With M = 256 (the pages' default slot count) the chunk tiles do not fit in LDS and the
+ * call evaluates the recurrence token by token instead (the recurrent form the README
+ * names for generation): the router over all rows, then one workgroup per head and column
+ * tile that keeps its part of H in registers; C is then only validated.  T < 2^31.
  */
 int rsm_forward_chunked(const void* q, const void* k, const void* z, const void* v, int dtype,
                         const float* f, const float* H0, int64_t B, int64_t T, int64_t Hh,

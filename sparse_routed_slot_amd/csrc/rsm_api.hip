@@ -69,7 +69,7 @@ const char* rsm_status_string(int status) {
     return "unknown status";
 }
 
-int rsm_abi_version(void) { return 10100; }
+int rsm_abi_version(void) { return 10200; }
 
 int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t K,
                    int32_t* idx, float* score, void* stream) {
@@ -97,9 +97,10 @@ int rsm_route_topk_ex(const void* z, int dtype, const rsm_router_opts* opts, int
 
 size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t Dv,
                                    int64_t C, int64_t K) {
-    if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv) || !c_ok(C)) return 0;
+    if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv) || !c_ok(C)) return 0;
     if (K < 1 || K > M) return 0;
     if (mul_ck({B, T + C, Hh, M, 5}) < 0 || mul_ck({B, Hh, T / C + 2, M, Dv, 4}) < 0) return 0;
+    if (M == 256) return rsm::forward_recurrent_workspace(long(B), long(T), long(Hh), int(K));
     return rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C), int(K)).total;
 }
 
@@ -118,11 +119,13 @@ int rsm_forward_chunked_ex(const void* q, const void* k, const void* z, const vo
     rsm::RouterOpts op;
     if (!router_opts(opts, op)) return RSM_ERR_UNSUPPORTED;
     if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
-    if (B < 0 || T < 0 || Hh < 0 || !m_ok(M) || !dv_ok(Dv) || !c_ok(C)) return RSM_ERR_SHAPE;
+    if (B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv) || !c_ok(C)) return RSM_ERR_SHAPE;
     if (K < 1 || K > M) return RSM_ERR_K;
     const int64_t rows = mul_ck({B, T, Hh});
     const int64_t heads = mul_ck({B, Hh});
     if (rows < 0 || heads < 0 || mul_ck({rows, M > Dv ? M : Dv}) < 0) return RSM_ERR_SHAPE;
+    // recurrent form (M = 256): token indices mark slots as int, the router grid is rows / 4
+    if (M == 256 && (T >= (int64_t(1) << 31) || rows / 4 >= (int64_t(1) << 31))) return RSM_ERR_SHAPE;
     const int64_t nbhc = heads * ((T + C - 1) / C);
     if (nbhc >= (int64_t(1) << 31) || heads * (Dv / 16) >= (int64_t(1) << 31)) return RSM_ERR_SHAPE;
     if (heads == 0) return RSM_OK;

@@ -240,6 +240,19 @@ __device__ __forceinline__ typename RowKey<T>::type row_threshold(const float (&
 }
 
 
+// Workgroup barrier without a memory fence.  A workgroup-scope release fence would also
+// wait for every global load still in flight (prefetches, direct global->LDS loads), which
+// the kernels wait for only where they use them.  LDS is coherent inside the workgroup, so
+// each wave's own LDS accesses having completed (lgkmcnt = 0) before s_barrier is what
+// makes them visible.  The signal fences keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // MFMA fragment types (16x16 output tiles).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));

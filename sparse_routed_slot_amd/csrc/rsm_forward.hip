@@ -131,6 +131,9 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
         hipLaunchKernelGGL(copy_state_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, H0, H_out, n);
         return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
     }
+    if (M == 256)  // chunk tiles of 256 slots do not fit in LDS: the recurrent form
+        return forward_recurrent_launch(q, k, z, v, dtype, f, H0, B, T, Hh, M, Dv, K, o, H_out, idx_out, workspace, op,
+                                        stream);
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     auto* rmask = reinterpret_cast<unsigned long long*>(ws + L.rmask_off);

@@ -46,6 +46,13 @@ int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, l
                      int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
                      hipStream_t stream);
 
+// Forward in the recurrent form (M = 256): the router over all rows into the workspace (or
+// idx_out), then one workgroup per (head, column tile) walks the tokens in order.
+size_t forward_recurrent_workspace(long B, long T, long Hh, int K);
+int forward_recurrent_launch(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
+                             const float* H0, long B, long T, long Hh, int M, int Dv, int K, float* o, float* H_out,
+                             int32_t* idx_out, void* workspace, const RouterOpts& op, hipStream_t stream);
+
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,
                            int Dv, int K, int C, float* o, float* H_out, int32_t* idx_out,

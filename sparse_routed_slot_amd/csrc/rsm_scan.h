@@ -350,18 +350,6 @@ __device__ __forceinline__ void wait_vm() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Workgroup barrier without a memory fence.  A workgroup-scope release fence would also
-// wait for every direct global->LDS load still in flight; the scan waits for those
-// explicitly, one chunk later.  LDS is coherent inside the workgroup, so each wave's own
-// LDS accesses having completed (lgkmcnt = 0) before s_barrier is what makes them visible.
-// The signal fences keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void wg_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Inclusive product scan across the 64 lanes of a wave (lane order): DPP row shifts by 1, 2,
 // 4, 8 within rows of 16 lanes, then row broadcasts of lane 15 and lane 31.  Lanes without a
 // source lane in a step multiply by 1 (the "old" operand of the DPP move).

@@ -81,7 +81,7 @@ def test_forward_argument_errors(lib):
     assert fwd(lib, dtype=3) == DTYPE
     assert fwd(lib, Dv=48) == SHAPE
     assert fwd(lib, C=48) == SHAPE
-    assert fwd(lib, M=256) == SHAPE
+    assert fwd(lib, M=512) == SHAPE
     assert fwd(lib, T=-5) == SHAPE
     assert fwd(lib, K=0) == KERR
     assert fwd(lib, q=None) == NULL
@@ -111,6 +111,10 @@ def test_workspace_size(lib):
     # enough heads for the whole chip: one segment, the route only
     assert f(1, 64, 2048, 8, 64, 128, 64, 16) < 64 * 2048 * 8 * (8 + 16 * 4) + 4096
     assert f(0, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * (8 + 16 * 4)
+    # M = 256 (recurrent form): the router's K indices and K weights per token-head
+    assert f(1, 16, 2048, 4, 256, 256, 64, 32) == 2 * 16 * 2048 * 4 * 32 * 4
+    assert f(1, 1, 3, 1, 256, 64, 64, 5) == 2 * 256                  # each part 256-byte aligned
+    assert f(1, 1, 0, 1, 256, 64, 64, 5) == 0
 
 
 def dec(lib, dtype=1, B=4, Hh=2, M=64, Dv=128, K=8, H=F_, o=G_, idx=None, q=A):
@@ -123,7 +127,8 @@ def test_decode_argument_errors(lib):
     assert dec(lib, M=512) == SHAPE
     assert dec(lib, M=256, Hh=0) == OK                 # the router and decode take M = 256
     assert route(lib, M=256, B=0) == OK and route(lib, M=512) == SHAPE
-    assert fwd(lib, M=256) == SHAPE                    # the chunked forward does not
+    assert fwd(lib, M=256, B=0) == OK                  # so does the forward (recurrent form)
+    assert fwd(lib, M=256, ws=None) == WS and fwd(lib, M=256, K=257) == KERR
     assert dec(lib, Dv=96) == SHAPE
     assert dec(lib, K=65) == KERR
     assert dec(lib, H=None) == NULL
@@ -168,4 +173,4 @@ def test_variant_argument_errors(lib):
     per_slot = RouterOpts(0, 0, 1, None)
     assert fw(ctypes.byref(per_slot), o=P(0x50000 + 100 * 2 * 4)) == ALIAS
     assert lib.rsm_route_topk_ex(A, 1, None, 0, 4, 2, 64, 4, B_, None, None) == OK
-    assert lib.rsm_abi_version() == 10100
+    assert lib.rsm_abi_version() == 10200

@@ -324,6 +324,7 @@ VAR_SHAPES = [  # dtype, B, T, Hh, M, Dv, K, C
     ("f32", 1, 130, 2, 32, 32, 8, 32),
     ("bf16", 1, 90, 2, 128, 64, 24, 32),
     ("bf16", 2, 77, 2, 16, 16, 16, 16),
+    ("bf16", 1, 70, 2, 256, 64, 32, 64),   # M = 256: recurrent form
 ]
 
 
@@ -445,3 +446,47 @@ def test_variant_route_wide_rows(rsm, var, dtype):
                                   score=score, normalize=normalize)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     np.testing.assert_allclose(sc.cpu().numpy(), rsc, rtol=2e-5, atol=1e-7)
+
+
+# ------------------------------------------------ forward at M = 256 (recurrent form)
+M256_CASES = [  # dtype, B, T, Hh, Dv, K, h0, f = -inf tokens
+    ("bf16", 2, 70, 2, 64, 32, False, False),
+    ("bf16", 1, 150, 2, 256, 32, True, True),    # four column tiles, T not a multiple of 4
+    ("f32", 1, 33, 1, 16, 100, True, False),     # K > 64: several route entries per lane
+    ("f32", 1, 5, 3, 32, 256, False, False),     # K = M: every slot every token
+    ("bf16", 3, 1, 2, 128, 8, True, False),      # one token
+]
+
+
+@pytest.mark.parametrize("case", M256_CASES, ids=_vid)
+def test_forward_m256(rsm, case):
+    dtype, B, T, Hh, Dv, K, h0, neg_inf = case
+    log(f"forward M256 {case}")
+    d = gen.make_inputs(B, T, Hh, 256, Dv, dtype, seed=zlib.crc32(repr(case).encode()) % 1000, h0=h0)
+    if neg_inf:
+        d["f"][:, T // 3: T // 3 + 7] = -np.inf
+    o, H, idx = run_forward(rsm, d, K, 64)
+    compare_forward(d, K, o, H, idx, what=f"M256 {case}")
+    if h0:  # slots never selected keep their initial rows bit for bit
+        never = np.ones((B, Hh, 256), dtype=bool)
+        for b in range(B):
+            for h in range(Hh):
+                never[b, h, np.unique(idx[b, :, h, :])] = False
+        assert np.array_equal(H[never], d["H0"][never])
+
+
+def test_forward_m256_inplace_and_empty(rsm):
+    log("forward M256: H_out = H0 in place, and T = 0")
+    d = gen.make_inputs(2, 40, 2, 256, 64, "bf16", seed=5, h0=True)
+    t = dev_inputs(d, "cuda")
+    H = t["H0"].clone()
+    o, H2, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], 32, H0=H, state_out=H,
+                                     want_idx=True)
+    torch.cuda.synchronize()
+    assert H2.data_ptr() == H.data_ptr()
+    compare_forward(d, 32, o.cpu().numpy(), H.cpu().numpy(), idx.cpu().numpy(), what="M256 in place")
+    e = gen.make_inputs(2, 0, 2, 256, 64, "bf16", seed=6, h0=True)
+    te = dev_inputs(e, "cuda")
+    o0, H0o, _ = rsm.forward_chunked(te["q"], te["k"], te["z"], te["v"], te["f"], 32, H0=te["H0"])
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and np.array_equal(H0o.cpu().numpy(), e["H0"])
