@@ -290,6 +290,31 @@ def main():
     print(f"[bench] decode, default layer shape (B{LB} Hh{LHh} M{LM} Dv{LDv} K{LK}): {dl_us:.2f} us/step, "
           f"{dl_bytes / (dl_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # forward at the pages' default layer shape (M = 256: the recurrent form)
+    FB, FT, FHh, FM, FDv, FK = 16, 2048, 4, 256, 256, 32
+    fl = to_dev(gen.make_inputs(FB, FT, FHh, FM, FDv, "bf16", 11), torch)
+    fo = torch.empty((FB, FT, FHh, FDv), dtype=torch.float32, device="cuda")
+    fH = torch.empty((FB, FHh, FM, FDv), dtype=torch.float32, device="cuda")
+    fws = torch.empty(rsm.forward_workspace_bytes(torch.bfloat16, FB, FT, FHh, FM, FDv, 64, FK), dtype=torch.uint8,
+                      device="cuda")
+
+    def fwd_layer():
+        rsm.forward_chunked(fl["q"], fl["k"], fl["z"], fl["v"], fl["f"], FK, workspace=fws, out=fo, state_out=fH)
+
+    fwd_layer()
+    torch.cuda.synchronize()
+    n_fl = 5
+    e0.record(stream)
+    for _ in range(n_fl):
+        fwd_layer()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fl_us = e0.elapsed_time(e1) * 1e3 / n_fl
+    fl_bytes = forward_bytes(FB, FT, FHh, FM, FDv, 2)
+    print(f"[bench] forward, default layer shape (B{FB} T{FT} Hh{FHh} M{FM} Dv{FDv} K{FK}, recurrent form): "
+          f"{fl_us:.0f} us/call, {FB * FT / fl_us:.2f} M tok/s", file=sys.stderr, flush=True)
+    del fl, fo, fH, fws
+
     rec = {
         "metric": METRIC,
         "value": tok / (ms_per_step * 1e-3),
@@ -322,6 +347,13 @@ def main():
                                  "us_per_step": dl_us, "algorithmic_bytes_per_launch": dl_bytes,
                                  "achieved": dl_bytes / (dl_us * 1e-6) / 1e9, "unit": "GB/s",
                                  "frac": dl_bytes / (dl_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "forward_default_layer": {"config": {"B": FB, "T": FT, "Hh": FHh, "M": FM, "Dv": FDv, "K": FK,
+                                             "form": "recurrent (router over all rows, then one workgroup per "
+                                                     "head and column tile walks the tokens)"},
+                                  "us_per_call": fl_us, "tokens_per_s": FB * FT / (fl_us * 1e-6),
+                                  "algorithmic_bytes_per_launch": fl_bytes,
+                                  "achieved": fl_bytes / (fl_us * 1e-6) / 1e9, "unit": "GB/s",
+                                  "frac": fl_bytes / (fl_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
         "variants": {
             "router": "softmax scores renormalised over the selected slots and per-slot decay rates; "
                       "the training line and the decode add fp32 exploration noise on the logits",
