@@ -325,6 +325,7 @@ VAR_SHAPES = [  # dtype, B, T, Hh, M, Dv, K, C
     ("bf16", 1, 90, 2, 128, 64, 24, 32),
     ("bf16", 2, 77, 2, 16, 16, 16, 16),
     ("bf16", 1, 70, 2, 256, 64, 32, 64),   # M = 256: recurrent form
+    ("f32", 1, 45, 2, 256, 32, 100, 64),   # M = 256, K > 64 (several route entries per lane)
 ]
 
 
@@ -485,6 +486,11 @@ def test_forward_m256_inplace_and_empty(rsm):
     torch.cuda.synchronize()
     assert H2.data_ptr() == H.data_ptr()
     compare_forward(d, 32, o.cpu().numpy(), H.cpu().numpy(), idx.cpu().numpy(), what="M256 in place")
+    o_ns, H_ns, _ = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], 32, H0=t["H0"], want_state=False)
+    torch.cuda.synchronize()
+    assert H_ns is None
+    ro, _, _ = oracle.forward(*(gen.as_f64(d[n], "bf16") for n in "qkzv"), d["f"], 32, H0=d["H0"])
+    check_close(o_ns.cpu().numpy(), ro, float(np.max(np.abs(ro))), TOL["bf16"], "M256 without state output")
     e = gen.make_inputs(2, 0, 2, 256, 64, "bf16", seed=6, h0=True)
     te = dev_inputs(e, "cuda")
     o0, H0o, _ = rsm.forward_chunked(te["q"], te["k"], te["z"], te["v"], te["f"], 32, H0=te["H0"])
