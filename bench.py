@@ -30,8 +30,8 @@ METRIC = "RSM forward tokens/s (B8 T2048 M64) + decode-step µs; % HBM/MFMA roof
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 # Sources of the forward kernels; the stored counter figures hold only for these bytes.
-FWD_SOURCES = ["rsm_forward.hip", "rsm_route.hip", "rsm_scan.h", "rsm_scan_args.h", "rsm_scan_bf16_m64.hip",
-               "rsm_device.h", "rsm_launch.h"]
+FWD_SOURCES = ["rsm_forward.hip", "rsm_route.hip", "rsm_route_row.h", "rsm_scan.h", "rsm_scan_args.h",
+               "rsm_scan_bf16_m64.hip", "rsm_device.h", "rsm_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_fwd_b8_t2048_traffic.txt")
 
 
@@ -335,9 +335,10 @@ def main():
                           "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": n_pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "kernel": "rsm_forward_chunked call = route_rows_kernel + fwd_scan_kernel pass A + "
-                               "fwd_scan_kernel pass B (three launches back to back on the caller's stream; "
-                               "the segment fold runs inside pass B at 4 segments)",
+                     "kernel": "rsm_forward_chunked call = fwd_scan_kernel pass A (routing its own segments, "
+                               "plus one route-only workgroup per head for the last segment) + fwd_scan_kernel "
+                               "pass B (two launches back to back on the caller's stream; the segment fold runs "
+                               "inside pass B at 4 segments)",
                      "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,

@@ -39,6 +39,7 @@
 #include "rsm_device.h"
 #include "rsm_launch.h"
 #include "rsm_scan_args.h"
+#include "rsm_route_row.h"
 
 namespace rsm {
 
@@ -469,11 +470,18 @@ constexpr int tri_row(int s) {
 template <bool PASS_A, int M>
 constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
 
-template <typename T, int M, int C, int DT, bool PASS_A>
+// FUSE (pass A only, default router, K <= 16, one Dv tile per head): the pass routes the
+// tokens itself -- each workgroup its own segment before the walk, and one extra workgroup
+// per head (past the scan's grid) the last segment, which pass B alone reads -- in place of
+// the separate router kernel; z, f and idx_out are the router's inputs and optional output.
+// (rmask and ralpha carry no __restrict__: the fused pass writes the route through them.)
+template <typename T, int M, int C, int DT, bool PASS_A, bool FUSE>
 __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
-    long T_len, int Hh, int Dv, int K, SegArgs sg, const unsigned long long* __restrict__ rmask,
-    const float* __restrict__ ralpha, float* __restrict__ o, float* __restrict__ H_out) {
+    long T_len, int Hh, int Dv, int K, SegArgs sg, const unsigned long long* rmask,
+    const float* ralpha, float* __restrict__ o, float* __restrict__ H_out, const T* __restrict__ z,
+    const float* __restrict__ f, int32_t* __restrict__ idx_out) {
+    static_assert(!FUSE || PASS_A, "only the first pass routes");
     typedef Pol<T> P;
     typedef typename P::E E;
     typedef typename P::frag frag;
@@ -531,7 +539,25 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     // segment) land on the same XCD (workgroups are dealt to the 8 XCDs round-robin)
     const int nDT = Dv / DT;
     const int nseg = PASS_A ? sg.S - 1 : sg.S;
-    const long nblk = gridDim.x;
+    long nblk = gridDim.x;
+    // routing segment sgi of head bhr: one token per thread, rows past the sequence end skipped
+    auto route_segment = [&](long bhr, long sgi) {
+        const long t_lo = sgi * sg.cps * C;
+        const long t_end = (sgi + 1) * sg.cps * C;
+        const long t_hi = t_end < T_len ? t_end : T_len;
+        const long hb = bhr / Hh, hh = bhr % Hh;
+        for (long t = t_lo + long(threadIdx.x); t < t_hi; t += 64 * NW)
+            route_row<T, M, true, true>(z, f, (hb * T_len + t) * Hh + hh, bhr, t, sg.nC * C, K, C, idx_out, nullptr,
+                                        const_cast<unsigned long long*>(rmask), const_cast<float*>(ralpha));
+    };
+    if constexpr (FUSE) {
+        const long heads = nblk / (long(nseg) * nDT + 1);
+        nblk -= heads;
+        if (long(blockIdx.x) >= nblk) {  // route-only workgroup: the last segment of one head
+            route_segment(long(blockIdx.x) - nblk, sg.S - 1);
+            return;
+        }
+    }
     long id = blockIdx.x;
     if (nblk % 8 == 0) id = (long(blockIdx.x) % 8) * (nblk / 8) + long(blockIdx.x) / 8;
     const int dtile = int(id % nDT);
@@ -1056,6 +1082,15 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
                     for (int r = 0; r < 4; ++r) dst[(16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16] = Hreg[j][I][r];
         }
     };
+    if constexpr (FUSE) {
+        // this segment's route, written before the walk's direct loads read it: each wave's
+        // stores acknowledged (vmcnt 0), then the barrier.  Within one workgroup that is
+        // enough: the vector L1 is write-through and holds none of these lines yet (an
+        // agent-scope fence would also write back the L2, once per workgroup).
+        route_segment(bh, seg);
+        wait_vm<0>();
+        __syncthreads();
+    }
     if constexpr (SPLIT) {
         if (mwave) run(std::true_type{}, std::false_type{});
         else run(std::false_type{}, std::true_type{});
@@ -1068,21 +1103,27 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
 template <typename T, int M, int C, int DT>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
                        int K, const SegArgs& sg, const unsigned long long* rmask, const float* ralpha, float* o,
-                       float* H_out, hipStream_t s) {
+                       float* H_out, const void* zr, const float* f, int32_t* idx_out, bool fuse, hipStream_t s) {
     const long tiles = B * Hh * (Dv / DT);
+    const T* z = static_cast<const T*>(zr);
     if (sg.S > 1) {
-        hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true>), dim3(unsigned(tiles * (sg.S - 1))),
-                           dim3(64 * scan_waves<true, M>()), 0, s,
-                           q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
+        if (fuse)  // pass A routes: one more workgroup per head for the last segment
+            hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, true>),
+                               dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<true, M>()), 0, s,
+                               q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
+        else
+            hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false>), dim3(unsigned(tiles * (sg.S - 1))),
+                               dim3(64 * scan_waves<true, M>()), 0, s,
+                               q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
         if (sg.S > kFoldMax + 1) {
             const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);
             if (st != RSM_OK) return st;
         }
     }
-    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false>), dim3(unsigned(tiles * sg.S)),
+    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false, false>), dim3(unsigned(tiles * sg.S)),
                        dim3(64 * scan_waves<false, M>()), 0, s, q, k, v,
-                       H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out);
+                       H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
@@ -1091,7 +1132,8 @@ template <typename T, int M, int C>
 static int dispatch_dt(int DT, const ScanArgs& a) {
     const T *q = static_cast<const T*>(a.q), *k = static_cast<const T*>(a.k), *v = static_cast<const T*>(a.v);
 #define RSM_SCAN(DTV) \
-    return launch_scan<T, M, C, DTV>(q, k, v, a.H0, a.B, a.T_len, a.Hh, a.Dv, a.K, a.sg, a.rmask, a.ralpha, a.o, a.H_out, a.s)
+    return launch_scan<T, M, C, DTV>(q, k, v, a.H0, a.B, a.T_len, a.Hh, a.Dv, a.K, a.sg, a.rmask, a.ralpha, a.o, \
+                                     a.H_out, a.z, a.f, a.idx_out, a.fuse_route, a.s)
     constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);
     switch (DT) {
         case 16: RSM_SCAN(16);

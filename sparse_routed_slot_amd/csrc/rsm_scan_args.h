@@ -26,6 +26,12 @@ struct ScanArgs {
     const float* ralpha;
     float *o, *H_out;
     hipStream_t s;
+    // the router's inputs and optional idx output, used when the first pass routes
+    // (fuse_route: default router, K <= 16, one Dv tile per head, more than one segment)
+    const void* z;
+    const float* f;
+    int32_t* idx_out;
+    bool fuse_route;
 };
 
 // Between the two passes: dH_s <- H_start(s+1) = diag(E_s) H_start(s) + dH_s for s = 0 .. S-2,
