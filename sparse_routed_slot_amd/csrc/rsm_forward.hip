@@ -141,8 +141,8 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
     const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),
                      reinterpret_cast<float*>(ws + L.de_off)};
     // With more than one segment and one Dv tile per head the first pass routes its own
-    // segments (default router, K <= 16); otherwise the router kernel runs first.
-    const bool fuse = op.is_default() && K <= 16 && L.S > 1 && L.dt == Dv;
+    // segments (bf16 inputs, default router, K <= 16); otherwise the router kernel runs first.
+    const bool fuse = dtype == RSM_BF16 && op.is_default() && K <= 16 && L.S > 1 && L.dt == Dv;
     if (!fuse) {
         const int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.chunk, idx_out, rmask,
                                         ralpha, op, stream);

@@ -470,7 +470,7 @@ constexpr int tri_row(int s) {
 template <bool PASS_A, int M>
 constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
 
-// FUSE (pass A only, default router, K <= 16, one Dv tile per head): the pass routes the
+// FUSE (pass A only, bf16 inputs, default router, K <= 16, one Dv tile per head): the pass routes the
 // tokens itself -- each workgroup its own segment before the walk, and one extra workgroup
 // per head (past the scan's grid) the last segment, which pass B alone reads -- in place of
 // the separate router kernel; z, f and idx_out are the router's inputs and optional output.
@@ -1107,11 +1107,16 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
     const long tiles = B * Hh * (Dv / DT);
     const T* z = static_cast<const T*>(zr);
     if (sg.S > 1) {
-        if (fuse)  // pass A routes: one more workgroup per head for the last segment
-            hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, true>),
-                               dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<true, M>()), 0, s,
-                               q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
-        else
+        bool routed = false;
+        if constexpr (std::is_same<T, bf16_t>::value) {  // fp32 rows would spill in the pass
+            if (fuse) {  // pass A routes: one more workgroup per head for the last segment
+                hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, true>),
+                                   dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<true, M>()), 0,
+                                   s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
+                routed = true;
+            }
+        }
+        if (!routed)
             hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false>), dim3(unsigned(tiles * (sg.S - 1))),
                                dim3(64 * scan_waves<true, M>()), 0, s,
                                q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);

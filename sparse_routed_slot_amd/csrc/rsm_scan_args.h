@@ -27,7 +27,8 @@ struct ScanArgs {
     float *o, *H_out;
     hipStream_t s;
     // the router's inputs and optional idx output, used when the first pass routes
-    // (fuse_route: default router, K <= 16, one Dv tile per head, more than one segment)
+    // (fuse_route: bf16 inputs, default router, K <= 16, one Dv tile per head, more than one
+    // segment)
     const void* z;
     const float* f;
     int32_t* idx_out;
