@@ -44,8 +44,10 @@
  *    README configuration table is a diagonal gate, paper summary section 2.1).
  *  - exploration noise: g [B,T,Hh,M] added to the logits before selection and scoring
  *    (paper summary section 6.2.2, Gumbel noise during training).  The caller draws g.
- *    The noisy logit is the fp32 sum fl32(z + g) -- the precision in which the GPU path
- *    forms it -- so both sides rank the same numbers.
+ *    The noisy logit is part of the input's definition: z and g are handed over as fp32
+ *    tensors, and the logit the router ranks and scores is their fp32 sum fl32(z + g),
+ *    the tensor a caller holding both in fp32 forms before routing.  The oracle builds
+ *    that input exactly (one fp32 add) and works in float64 from there.
  */
 #include <math.h>
 #include <stdint.h>
@@ -75,7 +77,7 @@ typedef struct {
     int normalize;
 } oracle_router;
 
-/* Logits of one row as the router ranks them: z, or fl32(z + g) with exploration noise. */
+/* Logits of one row as the router ranks them: z, or the noisy-logit input fl32(z + g). */
 static void oracle_logits(const double* z, const double* g, long M, double* zp) {
     for (long i = 0; i < M; ++i) zp[i] = g ? (double)((float)z[i] + (float)g[i]) : z[i];
 }

@@ -221,6 +221,8 @@ __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* 
                                           long t, long T_pad, int K, int C, int32_t* __restrict__ idx,
                                           float* __restrict__ score, unsigned long long* __restrict__ rmask,
                                           float* __restrict__ ralpha) {
+    // the walk over the selection mask below visits word 0, then word MW-1: at most two words
+    static_assert(M <= 128, "route_row covers at most 128 slots (the M = 256 router is route_wave_kernel)");
     typedef typename RowKey<T>::type U;
     RowRegs<T, M> x;
     x.load(z + row * M);

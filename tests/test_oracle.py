@@ -20,8 +20,17 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
 
 def _num(x):
+    """A number of the worked examples: a plain number, "-inf", a fraction "a/b", or
+    "[-][n]ln<m>" meaning -n*ln(m)."""
     if isinstance(x, str):
-        return {"-2ln2": -2.0 * math.log(2.0), "-inf": -math.inf}[x]
+        if x == "-inf":
+            return -math.inf
+        if "/" in x:
+            a, b = x.split("/")
+            return float(a) / float(b)
+        sign = -1.0 if x.startswith("-") else 1.0
+        n, m = x.lstrip("-").split("ln")
+        return sign * (float(n) if n else 1.0) * math.log(float(m))
     return float(x)
 
 
@@ -409,6 +418,49 @@ class TestVariants:
             assert idd[0, h].tolist() == sel
             np.testing.assert_allclose(od[0, h], out, rtol=1e-12, atol=1e-13)
             np.testing.assert_allclose(Hd[0, h], S, rtol=1e-12, atol=1e-13)
+
+
+class TestVariantWorkedExamples:
+    """Hand-worked values for the variants (tests/golden/worked_examples.json): per-slot
+    decay rates that differ across slots, so a rate taken by list position instead of by
+    slot index changes every value (GLA diagonal gate, README configuration table; paper
+    summary section 2.1); softmax scores renormalised over the selected slots (README
+    router_score option; paper summary sections 4.1 and 6.2.1)."""
+
+    @pytest.mark.parametrize("ex", json.load(open(GOLD))["variant_forward"], ids=lambda e: e["name"])
+    def test_forward_and_decode(self, ex):
+        M, Dv, K = ex["M"], ex["Dv"], ex["K"]
+        T = len(ex["z"])
+        arr = lambda key, n: np.array([[_num(x) for x in row] for row in ex[key]]).reshape(1, T, 1, n)
+        q, k, z, v = arr("q", M), arr("k", M), arr("z", M), arr("v", Dv)
+        if "f_slot" in ex:
+            f = arr("f_slot", M)
+        else:
+            f = np.array([_num(x) for x in ex["f"]]).reshape(1, T, 1)
+        H0 = np.array(ex["H0"], dtype=np.float64).reshape(1, 1, M, Dv)
+        kw = dict(score=ex["score"], normalize=ex["normalize"])
+        o, H, idx = oracle.forward(q, k, z, v, f, K, H0=H0, **kw)
+        np.testing.assert_allclose(o.reshape(T, Dv), np.array(ex["o"], dtype=np.float64), rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(H.reshape(M, Dv), np.array(ex["H_final"], dtype=np.float64),
+                                   rtol=1e-14, atol=1e-14)
+        assert idx.reshape(T, K).tolist() == ex["idx"]
+        Hs = H0.copy()
+        for t in range(T):
+            od, idd = oracle.decode_step(q[:, t], k[:, t], z[:, t], v[:, t], f[:, t], Hs, K, **kw)
+            np.testing.assert_allclose(od.reshape(Dv), np.array(ex["o"][t], dtype=np.float64),
+                                       rtol=1e-14, atol=1e-14)
+            assert idd.reshape(K).tolist() == ex["idx"][t]
+        np.testing.assert_allclose(Hs.reshape(M, Dv), np.array(ex["H_final"], dtype=np.float64),
+                                   rtol=1e-14, atol=1e-14)
+
+    @pytest.mark.parametrize("kind", ["sigmoid", "sigmoid_normalized", "softmax", "softmax_normalized"])
+    def test_route_weights(self, kind):
+        g = json.load(open(GOLD))["route_variants"]
+        z = np.array([[_num(x) for x in row] for row in g["z"]])
+        idx, w = oracle.route_topk(z, g["K"], score=kind.split("_")[0], normalize=kind.endswith("normalized"))
+        assert idx.tolist() == g["idx"]
+        want = np.array([[_num(x) for x in row] for row in g["weights"][kind]])
+        np.testing.assert_allclose(w, want, rtol=1e-15, atol=0)
 
 
 class TestGenerator:
