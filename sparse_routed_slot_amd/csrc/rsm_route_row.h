@@ -216,11 +216,15 @@ template <int M> struct RowRegs<float, M> {
 // run by the chunked forward's first pass when it routes its own segment).  kFwd: row is
 // the token-head row in (b, t, h) order, bh = b*Hh + h and t its token; outputs and layouts
 // as described above.  Public router: row only.
-template <typename T, int M, bool kFwd, bool SMALLK>
+// kCopy (forward router, K <= 16): also the token's mask words into cmask[0 .. MW-1] and its
+// alpha list in ascending slot order into clist[0 .. K-1] (a token-major copy for the caller).
+template <typename T, int M, bool kFwd, bool SMALLK, bool kCopy = false>
 __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* __restrict__ f, long row, long bh,
                                           long t, long T_pad, int K, int C, int32_t* __restrict__ idx,
                                           float* __restrict__ score, unsigned long long* __restrict__ rmask,
-                                          float* __restrict__ ralpha) {
+                                          float* __restrict__ ralpha, unsigned long long* cmask = nullptr,
+                                          float* clist = nullptr) {
+    static_assert(!kCopy || (kFwd && SMALLK), "the copy is a forward-router option for K <= 16");
     // the walk over the selection mask below visits word 0, then word MW-1: at most two words
     static_assert(M <= 128, "route_row covers at most 128 slots (the M = 256 router is route_wave_kernel)");
     typedef typename RowKey<T>::type U;
@@ -259,6 +263,10 @@ __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* 
         const long orow = bh * T_pad + t;
 #pragma unroll
         for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
+        if constexpr (kCopy) {
+#pragma unroll
+            for (int wd = 0; wd < MW; ++wd) cmask[wd] = mk[wd];
+        }
     }
     float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
     // walk the selected slots in ascending order (lowest set bit first); the logit of a
@@ -287,7 +295,9 @@ __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* 
             if (n < K) {
                 const float sc = sigmoidf_dev(zv[n]);
                 if (kFwd) {
-                    alist[long(n) * C] = sc > 0.0f ? __expf(sc * ft) : 1.0f;
+                    const float al = sc > 0.0f ? __expf(sc * ft) : 1.0f;
+                    alist[long(n) * C] = al;
+                    if constexpr (kCopy) clist[n] = al;
                     if (idx) idx[dst + n] = sl[n];
                 } else {
                     idx[dst + n] = sl[n];

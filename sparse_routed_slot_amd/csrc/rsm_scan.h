@@ -1100,6 +1100,12 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     if (PASS_A && dtile == 0 && tid < M) sg.dE[segrow + tid] = Eseg;
 }
 
+}  // namespace rsm
+
+#include "rsm_segstate.h"
+
+namespace rsm {
+
 template <typename T, int M, int C, int DT>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
                        int K, const SegArgs& sg, const unsigned long long* rmask, const float* ralpha, float* o,
@@ -1109,7 +1115,17 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
     if (sg.S > 1) {
         bool routed = false;
         if constexpr (std::is_same<T, bf16_t>::value) {  // fp32 rows would spill in the pass
-            if (fuse) {  // pass A routes: one more workgroup per head for the last segment
+            if constexpr (C >= 32) {
+                if (fuse) {  // segment states by the backward walk, which routes: one more workgroup
+                             // per head routes the last segment
+                    hipLaunchKernelGGL((seg_state_kernel<M, C, DT>), dim3(unsigned(B * Hh * sg.S)), dim3(512), 0, s,
+                                       reinterpret_cast<const bf16_t*>(k), reinterpret_cast<const bf16_t*>(v),
+                                       reinterpret_cast<const bf16_t*>(z), f, T_len, int(Hh), Dv, K, sg,
+                                       const_cast<unsigned long long*>(rmask), const_cast<float*>(ralpha), idx_out);
+                    routed = true;
+                }
+            }
+            if (fuse && !routed) {  // pass A routes: one more workgroup per head for the last segment
                 hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, true>),
                                    dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<true, M>()), 0,
                                    s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
