@@ -80,7 +80,8 @@ int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, i
  * The workspace holds the route of every token-head, padded to whole chunks (a selection
  * bit mask, 8 bytes per 64 slots, and the K decay factors of the selected slots, fp32),
  * and, when few heads make the forward cut each sequence into S segments, the fp32 end
- * state (M x Dv) and decay product (M) of every segment but the last, per head.  With
+ * state (M x Dv) and decay product (M) of every segment but the last, per head, plus room
+ * for a copy of H0 that an in-place call (H_out == H0) reads instead of H0.  With
  * M = 256 it holds the router's output instead: K slot indices (int32) and K weights (fp32)
  * per token-head.
  * Returns 0 for unsupported arguments as well; the forward call then reports the error.

@@ -104,6 +104,10 @@ FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int 
     off += align256(segs * size_t(M) * size_t(Dv) * 4);
     L.de_off = off;
     off += align256(segs * size_t(M) * 4);
+    // with segments, a copy of H0 for an in-place call (H_out == H0): the last segment writes
+    // H_out while workgroups of earlier segments may still read H0
+    L.h0c_off = off;
+    if (L.S > 1) off += align256(size_t(B) * size_t(Hh) * size_t(M) * size_t(Dv) * 4);
     L.total = off;
     return L;
 }
@@ -136,6 +140,13 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
                                         stream);
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if (H0 && H_out == H0 && L.S > 1) {  // in place: the passes read a copy of H0
+        float* h0c = reinterpret_cast<float*>(ws + L.h0c_off);
+        if (hipMemcpyAsync(h0c, H0, size_t(BH) * size_t(M) * size_t(Dv) * 4, hipMemcpyDeviceToDevice, stream) !=
+            hipSuccess)
+            return RSM_ERR_HIP;
+        H0 = h0c;
+    }
     auto* rmask = reinterpret_cast<unsigned long long*>(ws + L.rmask_off);
     auto* ralpha = reinterpret_cast<float*>(ws + L.ralpha_off);
     const SegArgs sg{L.n_chunks, L.S, L.cps, reinterpret_cast<float*>(ws + L.dh_off),

@@ -29,10 +29,12 @@ int decode_step_launch(const void* q, const void* k, const void* z, const void* 
 // Workspace of the chunked forward: the route of every token-head in (batch*head, padded
 // token) order -- a selection bit mask (uint64 words) and the alphas of the selected slots
 // (fp32, ascending slot order, slot-major within each chunk) -- then the state and decay
-// product of every sequence segment but the last; byte offsets and total.
+// product of every sequence segment but the last, and room for a copy of H0 (in-place calls
+// with segments); byte offsets and total.
 struct FwdLayout {
     size_t rmask_off, ralpha_off;  // route
     size_t dh_off, de_off;         // per-segment states and decay products (S > 1)
+    size_t h0c_off;                // copy of H0 for an in-place call (S > 1)
     size_t total;
     long n_chunks;
     int chunk;  // chunk length the kernels run

@@ -186,6 +186,27 @@ def test_forward_split_sequence_resumes(rsm):
     check_close(H2.cpu().numpy(), H.cpu().numpy().astype(np.float64), scale, TOL["bf16"], "split H")
 
 
+@pytest.mark.parametrize("case", [("bf16", 1, 8192, 3, 64, 128), ("bf16", 8, 1024, 8, 64, 128),
+                                  ("bf16", 2, 640, 2, 64, 128), ("f32", 1, 2048, 2, 32, 64)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_forward_inplace_state_with_segments(rsm, case):
+    """H_out is the H0 buffer while the sequence is cut into segments: workgroups of early
+    segments may start after the last segment's workgroup has written H_out, so the call
+    must read the initial state from a copy (128 segments folded by the fold kernel; 4
+    folded inside the second pass; 5; fp32)."""
+    dtype, B, T, Hh, M, Dv = case
+    K = 16 if M >= 32 else 4
+    log(f"in-place state with segments {case}")
+    d = gen.make_inputs(B, T, Hh, M, Dv, dtype, seed=zlib.crc32(repr(case).encode()) % 1000, h0=True)
+    t = dev_inputs(d, "cuda")
+    H = t["H0"].clone()
+    o, H2, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=64, H0=H, state_out=H,
+                                     want_idx=True)
+    torch.cuda.synchronize()
+    assert H2.data_ptr() == H.data_ptr()
+    compare_forward(d, K, o.cpu().numpy(), H.cpu().numpy(), idx.cpu().numpy(), what=f"in place {case}")
+
+
 def test_forward_empty(rsm):
     log("empty sequence")
     H0 = torch.randn(2, 3, 64, 128, device="cuda")
@@ -277,8 +298,10 @@ def test_prefill_then_decode_matches_longer_forward(rsm):
 
 def test_decode_workload_prefill_and_steps(rsm):
     """Batched decode: 256 sequences x 16 heads, M64 Dv128 K16; prefill T=512 by the
-    chunked forward, then single-token steps.  The oracle follows sampled sequences from
-    its own float64 prefill (end to end) and from the GPU's fp32 state (decode alone)."""
+    chunked forward, then all 1024 single-token steps, the run bench.py times.  On four
+    sampled sequences the oracle follows its own float64 prefill through every step (end to
+    end: o checked at every step, the state at steps 256, 512 and 1024), and at those
+    steps it also takes one step from the GPU's fp32 state (the decode kernel alone)."""
     log("decode workload: prefill")
     w = gen.WORKLOADS["decode_b256"]
     d = gen.make_workload("decode_b256")
@@ -287,6 +310,7 @@ def test_decode_workload_prefill_and_steps(rsm):
     o, H, idx = rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], K, C=w.C, want_idx=True)
     torch.cuda.synchronize()
     samp = np.array([0, 37, 128, 255])
+    samp_t = torch.from_numpy(samp).cuda()
     r = f64_inputs(d, samp)
     ro, rH, ridx = oracle.forward(r["q"], r["k"], r["z"], r["v"], r["f"], K)
     assert np.array_equal(idx.cpu().numpy()[samp], ridx)
@@ -294,21 +318,30 @@ def test_decode_workload_prefill_and_steps(rsm):
     check_close(o.cpu().numpy()[samp], ro, scale, TOL["bf16"], "prefill o")
     check_close(H.cpu().numpy()[samp], rH, scale, TOL["bf16"], "prefill H")
     rng = np.random.default_rng(1000 + w.seed)
-    Hgpu_from = H.cpu().numpy()[samp].astype(np.float64)
-    for step in range(16):
+    steps = w.extra["steps"]
+    checkpoints = {256, 512, steps}
+    worst = 0.0
+    for step in range(1, steps + 1):
         s = gen.decode_step_inputs(rng, w.B, w.Hh, w.M, w.Dv, "bf16")
         st = {n: to_torch(s[n], "bf16", "cuda") for n in "qkzv"}
+        args = [gen.as_f64(s[n][samp], "bf16") for n in "qkzv"] + [s["f"][samp].astype(np.float64)]
+        if step in checkpoints:  # the GPU state entering this step
+            Hgpu = H.index_select(0, samp_t).cpu().numpy().astype(np.float64)
         od, idd = rsm.decode_step(st["q"], st["k"], st["z"], st["v"], torch.from_numpy(s["f"]).cuda(), H, K,
                                   want_idx=True)
-        torch.cuda.synchronize()
-        args = [gen.as_f64(s[n][samp], "bf16") for n in "qkzv"] + [s["f"][samp].astype(np.float64)]
         o_e2e, i_e2e = oracle.decode_step(*args, rH, K)
-        o_dec, _ = oracle.decode_step(*args, Hgpu_from, K)
-        assert np.array_equal(idd.cpu().numpy()[samp], i_e2e)
+        od_s = od.index_select(0, samp_t).cpu().numpy()
+        assert np.array_equal(idd.index_select(0, samp_t).cpu().numpy(), i_e2e), f"decode step {step}: top-K"
         sc = float(np.max(np.abs(o_e2e)))
-        check_close(od.cpu().numpy()[samp], o_e2e, sc, TOL["bf16"], f"decode e2e step {step}")
-        check_close(od.cpu().numpy()[samp], o_dec, sc, TOL["bf16"], f"decode-only step {step}")
-        Hgpu_from = H.cpu().numpy()[samp].astype(np.float64)
+        e = check_close(od_s, o_e2e, sc, TOL["bf16"], f"decode e2e step {step}")
+        worst = max(worst, e / sc)
+        if step in checkpoints:
+            o_dec, _ = oracle.decode_step(*args, Hgpu, K)
+            check_close(od_s, o_dec, sc, TOL["bf16"], f"decode-only step {step}")
+            Hs = H.index_select(0, samp_t).cpu().numpy()
+            check_close(Hs, Hgpu, sc, TOL["bf16"], f"decode-only state step {step}")
+            eh = check_close(Hs, rH, sc, TOL["bf16"], f"decode e2e state step {step}")
+            log(f"decode step {step}: worst e2e o error so far {worst:.2e} of max|o|, state {eh / sc:.2e}")
 
 
 # ------------------------------------------------------------ router and decay variants
