@@ -54,7 +54,8 @@ typedef enum {
     RSM_ERR_UNSUPPORTED = -5, /* a combination the library was not built for */
     RSM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the queried size */
     RSM_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
-    RSM_ERR_ALIAS = -8        /* an output overlaps an input it must not overlap */
+    RSM_ERR_ALIAS = -8,       /* an output overlaps an input it must not overlap */
+    RSM_ERR_TOO_LARGE = -9    /* the call needs more scratch than rsm_noalloc_scratch_bytes() */
 } rsm_status;
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -179,6 +180,22 @@ int rsm_decode_step_ex(const void* q, const void* k, const void* z, const void* 
                        const float* f, float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv,
                        int64_t K, float* o, int32_t* idx_out, const rsm_router_opts* opts,
                        void* stream);
+
+/*
+ * rsm_forward_chunked without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as rsm_forward_chunked, whose kernels it
+ * runs; the workspace is a fixed array inside the library (rsm_noalloc_scratch_bytes(),
+ * 64 MiB, one copy per device, held until the process ends).  A problem whose
+ * rsm_forward_workspace_bytes() exceeds it returns RSM_ERR_TOO_LARGE before anything is
+ * enqueued.  The call allocates nothing.  Calls that overlap on one device (several streams
+ * or host threads) share that array and race: serialise them.
+ */
+size_t rsm_noalloc_scratch_bytes(void);
+int rsm_forward_chunked_noalloc(const void* q, const void* k, const void* z, const void* v,
+                                int dtype, const float* f, const float* H0, int64_t B, int64_t T,
+                                int64_t Hh, int64_t M, int64_t Dv, int64_t K, int64_t C, float* o,
+                                float* H_out, int32_t* idx_out, void* stream);
 
 #ifdef __cplusplus
 }

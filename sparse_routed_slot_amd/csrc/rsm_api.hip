@@ -65,11 +65,13 @@ const char* rsm_status_string(int status) {
         case RSM_ERR_WORKSPACE: return "workspace is NULL or smaller than rsm_forward_workspace_bytes()";
         case RSM_ERR_HIP: return "the HIP runtime reported an error at launch";
         case RSM_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
+        case RSM_ERR_TOO_LARGE:
+            return "the call needs more workspace than the fixed scratch array of the no-allocation entry point";
     }
     return "unknown status";
 }
 
-int rsm_abi_version(void) { return 10200; }
+int rsm_abi_version(void) { return 10300; }
 
 int rsm_route_topk(const void* z, int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t K,
                    int32_t* idx, float* score, void* stream) {

@@ -13,7 +13,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["RSMError", "lib_path", "load", "route_topk", "forward_chunked", "decode_step",
+__all__ = ["RSMError", "lib_path", "load", "route_topk", "forward_chunked", "forward_chunked_noalloc",
+           "noalloc_scratch_bytes", "decode_step",
            "forward_workspace_bytes", "abi_version", "DTYPE_CODES", "SCORE_KINDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,10 @@ def load():
     lib.rsm_forward_chunked_ex.restype = I
     lib.rsm_decode_step_ex.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I64, P, P, O, P]
     lib.rsm_decode_step_ex.restype = I
+    lib.rsm_noalloc_scratch_bytes.argtypes = []
+    lib.rsm_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.rsm_forward_chunked_noalloc.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P]
+    lib.rsm_forward_chunked_noalloc.restype = I
     _lib = lib
     return lib
 
@@ -177,6 +182,37 @@ def forward_chunked(q, k, z, v, f, K: int, C: int = 64, H0: Optional[torch.Tenso
         _check(load().rsm_forward_chunked_ex(
             _ptr(q), _ptr(k), _ptr(z), _ptr(v), _code(q), _ptr(f), _ptr(H0), B, T, Hh, M, Dv, K, C,
             _ptr(o), _ptr(H), _ptr(idx), _ptr(workspace), workspace.numel(), ctypes.byref(opts), _stream()))
+    return o, H, idx
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the library's fixed scratch array used by forward_chunked_noalloc."""
+    return int(load().rsm_noalloc_scratch_bytes())
+
+
+def forward_chunked_noalloc(q, k, z, v, f, K: int, C: int = 64, H0: Optional[torch.Tensor] = None,
+                            want_idx: bool = False, out: Optional[torch.Tensor] = None,
+                            state_out: Optional[torch.Tensor] = None):
+    """forward_chunked through rsm_forward_chunked_noalloc: the library allocates nothing;
+    its workspace is the library's fixed per-device scratch array.  out and state_out (and
+    the idx buffer, when want_idx) are the caller's; pass preallocated ones to allocate
+    nothing here either.  Returns (o, H_out, idx or None)."""
+    q, k, z, v, f = (_dev(t, n) for t, n in zip((q, k, z, v, f), "qkzvf"))
+    if not (q.dtype == k.dtype == z.dtype == v.dtype) or f.dtype != torch.float32:
+        raise ValueError("q, k, z, v must share one dtype; f must be float32")
+    B, T, Hh, M = q.shape
+    Dv = v.shape[-1]
+    if tuple(f.shape) != (B, T, Hh):
+        raise ValueError("f must be [B,T,Hh]")
+    if H0 is not None:
+        H0 = _dev(H0, "H0")
+    dev = q.device
+    o = out if out is not None else torch.empty((B, T, Hh, Dv), dtype=torch.float32, device=dev)
+    H = state_out if state_out is not None else torch.empty((B, Hh, M, Dv), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, Hh, K), dtype=torch.int32, device=dev) if want_idx else None
+    _check(load().rsm_forward_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(z), _ptr(v), _code(q), _ptr(f), _ptr(H0), B, T, Hh, M, Dv, K, C,
+        _ptr(o), _ptr(H), _ptr(idx), _stream()))
     return o, H, idx
 
 

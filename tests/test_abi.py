@@ -173,4 +173,4 @@ def test_variant_argument_errors(lib):
     per_slot = RouterOpts(0, 0, 1, None)
     assert fw(ctypes.byref(per_slot), o=P(0x50000 + 100 * 2 * 4)) == ALIAS
     assert lib.rsm_route_topk_ex(A, 1, None, 0, 4, 2, 64, 4, B_, None, None) == OK
-    assert lib.rsm_abi_version() == 10200
+    assert lib.rsm_abi_version() == 10300
