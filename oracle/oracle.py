@@ -49,6 +49,8 @@ def _load():
     lib.rsm_oracle_forward_ex.argtypes = [P, P, P, P, P, P, I, P, L, L, L, L, L, L, I, I, P, P, P, P, I]
     lib.rsm_oracle_decode_step.argtypes = [P, P, P, P, P, P, L, L, L, L, L, P, P, I]
     lib.rsm_oracle_decode_ex.argtypes = [P, P, P, P, P, P, I, P, L, L, L, L, L, I, I, P, P, I]
+    lib.rsm_oracle_backward.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, L, L, P, P, P, P, P, P, I]
+    lib.rsm_oracle_backward.restype = ctypes.c_int
     for fn in (lib.rsm_oracle_route_topk, lib.rsm_oracle_route_ex, lib.rsm_oracle_forward,
                lib.rsm_oracle_forward_ex, lib.rsm_oracle_decode_step, lib.rsm_oracle_decode_ex):
         fn.restype = ctypes.c_int
@@ -135,3 +137,23 @@ def decode_step(q, k, z, v, f, H, K: int, nthreads: int = 0, noise=None, score: 
     if rc != 0:
         raise ValueError(f"oracle decode_step failed ({rc})")
     return o, idx
+
+
+def backward(q, k, z, v, f, K: int, dO, H0=None, dHT=None, nthreads: int = 0):
+    """Float64 gradients of L = sum(dO * o) + sum(dHT * H_final) for the default router.
+    Shapes as forward(); dO [B,T,Hh,Dv], dHT [B,Hh,M,Dv] or None (zero).
+    Returns (dq, dk, dz, dv, df, dH0)."""
+    q, k, z, v, f, H0, dO, dHT = map(_f64, (q, k, z, v, f, H0, dO, dHT))
+    B, T, Hh, M = q.shape
+    Dv = v.shape[-1]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dz = np.empty_like(z)
+    dv = np.empty_like(v)
+    df = np.empty_like(f)
+    dH0 = np.empty((B, Hh, M, Dv), dtype=np.float64)
+    rc = _load().rsm_oracle_backward(_p(q), _p(k), _p(z), _p(v), _p(f), _p(H0), _p(dO), _p(dHT), B, T, Hh, M, Dv,
+                                     K, _p(dq), _p(dk), _p(dz), _p(dv), _p(df), _p(dH0), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle backward failed ({rc})")
+    return dq, dk, dz, dv, df, dH0

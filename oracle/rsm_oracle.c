@@ -261,6 +261,112 @@ int rsm_oracle_decode_step(const double* q, const double* k, const double* z, co
                                 nthreads);
 }
 
+/* Gradients of the default-router recurrence (sigmoid scores, one decay rate per token-head)
+ * for the loss L = sum(dO . o) + sum(dH_T . H_T), i.e. the vector-Jacobian product with the
+ * upstream gradients dO [B,T,Hh,Dv] and dHT [B,Hh,M,Dv] (NULL = 0).  Outputs (all written):
+ * dq, dk, dz [B,T,Hh,M], dv [B,T,Hh,Dv], df [B,T,Hh], dH0 [B,Hh,M,Dv].
+ *
+ * Per (b, h) the forward runs first and keeps every state H_t (the state after token t,
+ * H_{-1} = H0).  The backward then walks t = T-1 .. 0 carrying G = dL/dH_t, written out from
+ * the chain rule on the update of the README listing, H_t[i,:] = a_i H_{t-1}[i,:] +
+ * (1 - a_i) k_i v_t for the selected slots (a_i = exp(s_i f_t), s_i = sigmoid(z_i)), and the
+ * read o_t = q_t . H_t:
+ *   G        += q_t (x) dO_t                       (the read of token t)
+ *   dq_t[i]   = sum_c dO_t[c] H_t[i,c]
+ *   for every selected slot i with s_i > 0:
+ *     dk_t[i]   = (1 - a_i) sum_c G[i,c] v_t[c]
+ *     dv_t[c]  += (1 - a_i) k_i G[i,c]
+ *     da        = sum_c G[i,c] (H_{t-1}[i,c] - k_i v_t[c])
+ *     dg        = a_i da                          (a = exp(g), g = s_i f_t)
+ *     df_t     += dg s_i,   dz_t[i] = dg f_t s_i (1 - s_i)
+ *     G[i,:]   *= a_i                             (what flows to H_{t-1})
+ *   dH0 = G after token 0.
+ * The top-K selection is piecewise constant in z, so an unselected slot gets dz = 0 and passes
+ * G through unchanged.  A selected slot whose score is 0 (sigmoid underflow) is frozen: no
+ * gradient.  With a = 0 (f = -inf, or exp underflow) a does not move with s or f, so dg = 0
+ * (no df or dz contribution) while dk, dv and the cut of G still apply. */
+int rsm_oracle_backward(const double* q, const double* k, const double* z, const double* v,
+                        const double* f, const double* H0, const double* dO, const double* dHT,
+                        long B, long T, long Hh, long M, long Dv, long K, double* dq, double* dk,
+                        double* dz, double* dv, double* df, double* dH0, int nthreads) {
+    if (!q || !k || !z || !v || !f || !dO || !dq || !dk || !dz || !dv || !df || !dH0) return -1;
+    if (B < 1 || T < 0 || Hh < 1 || M < 1 || Dv < 1 || K < 1 || K > M) return -1;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long bh = 0; bh < B * Hh; ++bh) {
+        long b = bh / Hh, h = bh % Hh;
+        double* Hs = (double*)malloc(sizeof(double) * (size_t)((T + 1) * M * Dv)); /* H_{t-1}, t = 0..T */
+        double* sc = (double*)malloc(sizeof(double) * (size_t)(T * M));            /* s, 0 if unselected */
+        double* G = (double*)malloc(sizeof(double) * (size_t)(M * Dv));
+        unsigned char* sel = (unsigned char*)malloc((size_t)M);
+        double* w = (double*)malloc(sizeof(double) * (size_t)(2 * M));
+        double* orow = (double*)malloc(sizeof(double) * (size_t)Dv);
+        if (!Hs || !sc || !G || !sel || !w || !orow) {
+            free(Hs); free(sc); free(G); free(sel); free(w); free(orow);
+            status = -2;
+            continue;
+        }
+        /* forward, keeping every state: Hs + (t+1)*M*Dv holds H_t */
+        for (long i = 0; i < M * Dv; ++i) Hs[i] = H0 ? H0[bh * M * Dv + i] : 0.0;
+        const oracle_router rr = {0, 0};
+        for (long t = 0; t < T; ++t) {
+            long row = (b * T + t) * Hh + h;
+            double* Hn = Hs + (t + 1) * M * Dv;
+            memcpy(Hn, Hs + t * M * Dv, sizeof(double) * (size_t)(M * Dv));
+            oracle_token(q + row * M, k + row * M, z + row * M, NULL, v + row * Dv, f + row, 0, rr, Hn, M,
+                         Dv, K, 0, Dv, orow, NULL, sel, w);
+            for (long i = 0; i < M; ++i) sc[t * M + i] = sel[i] ? w[M + i] : 0.0;
+        }
+        /* backward */
+        for (long i = 0; i < M * Dv; ++i) G[i] = dHT ? dHT[bh * M * Dv + i] : 0.0;
+        for (long t = T - 1; t >= 0; --t) {
+            long row = (b * T + t) * Hh + h;
+            const double* qt = q + row * M;
+            const double* kt = k + row * M;
+            const double* vt = v + row * Dv;
+            const double* dOt = dO + row * Dv;
+            const double* Ht = Hs + (t + 1) * M * Dv;
+            const double* Hp = Hs + t * M * Dv;
+            for (long i = 0; i < M; ++i)
+                for (long c = 0; c < Dv; ++c) G[i * Dv + c] += qt[i] * dOt[c];
+            for (long i = 0; i < M; ++i) {
+                double acc = 0.0;
+                for (long c = 0; c < Dv; ++c) acc += dOt[c] * Ht[i * Dv + c];
+                dq[row * M + i] = acc;
+            }
+            for (long c = 0; c < Dv; ++c) dv[row * Dv + c] = 0.0;
+            double dft = 0.0;
+            for (long i = 0; i < M; ++i) {
+                double s = sc[t * M + i];
+                dk[row * M + i] = 0.0;
+                dz[row * M + i] = 0.0;
+                if (s == 0.0) continue; /* unselected, or frozen */
+                double a = exp(s * f[row]);
+                double u = 0.0, da = 0.0;
+                for (long c = 0; c < Dv; ++c) {
+                    u += G[i * Dv + c] * vt[c];
+                    da += G[i * Dv + c] * (Hp[i * Dv + c] - kt[i] * vt[c]);
+                }
+                dk[row * M + i] = (1.0 - a) * u;
+                for (long c = 0; c < Dv; ++c) dv[row * Dv + c] += (1.0 - a) * kt[i] * G[i * Dv + c];
+                if (a > 0.0) {
+                    double dg = a * da;
+                    dft += dg * s;
+                    dz[row * M + i] = dg * f[row] * s * (1.0 - s);
+                }
+                for (long c = 0; c < Dv; ++c) G[i * Dv + c] *= a;
+            }
+            df[row] = dft;
+        }
+        for (long i = 0; i < M * Dv; ++i) dH0[bh * M * Dv + i] = G[i];
+        free(Hs); free(sc); free(G); free(sel); free(w); free(orow);
+    }
+    return status;
+}
+
 int rsm_oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
