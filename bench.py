@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 # Sources of the forward kernels; the stored counter figures hold only for these bytes.
 FWD_SOURCES = ["rsm_forward.hip", "rsm_route.hip", "rsm_route_row.h", "rsm_scan.h", "rsm_scan_args.h",
-               "rsm_scan_bf16_m64.hip", "rsm_device.h", "rsm_launch.h"]
+               "rsm_segstate.h", "rsm_scan_bf16_m64.hip", "rsm_device.h", "rsm_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_fwd_b8_t2048_traffic.txt")
 
 
@@ -96,9 +96,138 @@ def cpu_baseline(w, d, min_seconds=10.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    return {"value": reps * w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x the full forward workload (B{w.B} T{w.T} Hh{w.Hh} M{w.M} Dv{w.Dv} "
-                      f"K{w.K}), float64 recurrence, {dt:.1f} s wall on {threads} threads"}
+    out = {"value": reps * w.B * w.T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} x the full forward workload (B{w.B} T{w.T} Hh{w.Hh} M{w.M} Dv{w.Dv} "
+                     f"K{w.K}), float64 recurrence, {dt:.1f} s wall on {threads} threads"}
+    # one core: a bounded sample (the first 256 tokens of one batch row, all heads)
+    sl = (slice(0, 1), slice(0, 256))
+    t0 = time.perf_counter()
+    oracle.forward(r["q"][sl], r["k"][sl], r["z"][sl], r["v"][sl], f[sl], w.K, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    out["one_core"] = {"value": 256 / dt1, "unit": "tokens/s", "cores": 1,
+                       "sample": f"B1 T256 Hh{w.Hh} of the same workload, {dt1:.2f} s"}
+    # decode: one oracle step of the batched decode workload (256 sequences x 16 heads)
+    wd = gen.WORKLOADS["decode_b256"]
+    rng = np.random.default_rng(5)
+    s = gen.decode_step_inputs(rng, wd.B, wd.Hh, wd.M, wd.Dv, "bf16")
+    H = rng.standard_normal((wd.B, wd.Hh, wd.M, wd.Dv))
+    args = [gen.as_f64(s[n], "bf16") for n in "qkzv"] + [s["f"].astype(np.float64)]
+    steps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 2.0:
+        oracle.decode_step(*args, H, wd.K)
+        steps += 1
+    dtd = (time.perf_counter() - t0) / steps
+    out["decode_us_per_step"] = {"value": dtd * 1e6, "cores": threads,
+                                 "sample": f"{steps} steps of B{wd.B} Hh{wd.Hh} M{wd.M} Dv{wd.Dv} K{wd.K}"}
+    return out
+
+
+def time_forward_workload(name, torch, gen, rsm, steps):
+    """One forward workload (every config besides the headline one): inputs generated once,
+    2 warm-up calls, then `steps` calls between two HIP events.  Working sets of 300 MB and
+    more exceed the last-level cache by themselves; the tiny one is launch-bound."""
+    w = gen.WORKLOADS[name]
+    d = gen.make_workload(name)
+    es = 4 if w.dtype == "f32" else 2
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    if w.dtype == "f32":
+        t = {n: torch.from_numpy(np.ascontiguousarray(d[n], np.float32)).cuda() for n in "qkzv"}
+    else:
+        t = {n: torch.from_numpy(np.ascontiguousarray(d[n]).view(np.int16)).view(torch.bfloat16).cuda()
+             for n in "qkzv"}
+    t["f"] = torch.from_numpy(d["f"]).cuda()
+    del d
+    o = torch.empty((w.B, w.T, w.Hh, w.Dv), dtype=torch.float32, device="cuda")
+    H = torch.empty((w.B, w.Hh, w.M, w.Dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, rsm.forward_workspace_bytes(tdt, w.B, w.T, w.Hh, w.M, w.Dv, w.C, w.K)),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        rsm.forward_chunked(t["q"], t["k"], t["z"], t["v"], t["f"], w.K, C=w.C, workspace=ws, out=o, state_out=H)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = forward_bytes(w.B, w.T, w.Hh, w.M, w.Dv, es)
+    c_run = 32 if (w.M == 128 and w.C > 32) else w.C
+    rec = {"config": {"B": w.B, "T": w.T, "Hh": w.Hh, "M": w.M, "Dv": w.Dv, "K": w.K, "C": w.C,
+                      "C_run": c_run, "dtype": w.dtype, "structure": w.note or "as the headline workload"},
+           "us_per_call": us, "tokens_per_s": w.B * w.T / (us * 1e-6), "algorithmic_bytes_per_launch": nbytes,
+           "achieved": nbytes / (us * 1e-6) / 1e9, "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    if name == "tiny_f32":
+        rec["note"] = "0.17 MB of data: launch-latency bound, absolute time only"
+    print(f"[bench] forward {name}: {us:.1f} us/call, {rec['achieved']:.0f} GB/s "
+          f"({rec['frac'] * 100:.1f}% of HBM peak), C run {c_run}", file=sys.stderr, flush=True)
+    del t, o, H, ws
+    return rec
+
+
+def backward_bytes(B, T, Hh, M, Dv, es):
+    """Algorithmic bytes of one backward: q, k, z, v, f, dO and dH_T read once; dq, dk, dz,
+    dv, df and dH0 written once."""
+    rows, heads = B * T * Hh, B * Hh
+    return (3 * rows * M * es + rows * Dv * es + rows * 4 + rows * Dv * 4 + heads * M * Dv * 4
+            + 3 * rows * M * 4 + rows * Dv * 4 + rows * 4 + heads * M * Dv * 4)
+
+
+def time_backward(w, s, torch, rsm, steps):
+    """rsm_backward on the headline workload (random upstream gradients), between HIP events."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    dO = torch.randn((w.B, w.T, w.Hh, w.Dv), device="cuda", generator=g)
+    dHT = torch.randn((w.B, w.Hh, w.M, w.Dv), device="cuda", generator=g)
+    ws = torch.empty(rsm.load().rsm_backward_workspace_bytes(1, w.B, w.T, w.Hh, w.M, w.Dv, w.K), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        return rsm.backward(s["q"], s["k"], s["z"], s["v"], s["f"], w.K, dO, dHT=dHT, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = backward_bytes(w.B, w.T, w.Hh, w.M, w.Dv, 2)
+    print(f"[bench] backward {w.name}: {us:.1f} us/call, {w.B * w.T / us:.2f} M tok/s, "
+          f"{nbytes / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    del dO, dHT, ws
+    return {"workload": w.name, "us_per_call": us, "tokens_per_s": w.B * w.T / (us * 1e-6),
+            "algorithmic_bytes_per_launch": nbytes, "achieved": nbytes / (us * 1e-6) / 1e9, "unit": "GB/s",
+            "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "form": "token-recurrent: route, rows forward (dq), rows backward (dk, dz, dg s, dH0), "
+                    "columns backward (dv), df sum; see the design notes"}
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Measured device-to-device copy rate (read + write bytes per second) of a 1 GiB buffer."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return {"bytes_moved_per_copy": 2 * nbytes, "GB_per_s": 2 * nbytes / s / 1e9,
+            "method": "torch copy_ of a 1 GiB fp32 buffer, 10 copies between HIP events"}
 
 
 def main():
@@ -108,6 +237,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the timing of the other forward configs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -263,7 +393,26 @@ def main():
     dvar_bytes = dbytes + variant_extra_bytes(wd.B * wd.Hh, wd.M)
     print(f"[bench] decode, router/decay variant: {dvar_us:.2f} us/step, "
           f"{dvar_bytes / (dvar_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
-    del vpool, pool, Hdec
+    # decode over a state that cannot stay in the 256 MB last-level cache: three state
+    # buffers (3 x 134 MB) rotated step by step
+    Hrot = [Hdec] + [Hdec.clone() for _ in range(2)]
+
+    def dec_rot(i):
+        s = pool[i % len(pool)]
+        rsm.decode_step(s["q"], s["k"], s["z"], s["v"], s["f"], Hrot[i % 3], wd.K, out=od)
+
+    for i in range(6):
+        dec_rot(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.decode_steps):
+        dec_rot(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    drot_us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    print(f"[bench] decode, 3 rotated states (402 MB, past the last-level cache): {drot_us:.2f} us/step, "
+          f"{dbytes / (drot_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    del vpool, pool, Hdec, Hrot
 
     # decode step at the pages' default layer shape (4 heads, 256 slots, top-32, head dim 256),
     # 256 sequences; the state is drawn at random (the chunked forward takes M <= 128)
@@ -315,6 +464,17 @@ def main():
           f"{fl_us:.0f} us/call, {FB * FT / fl_us:.2f} M tok/s", file=sys.stderr, flush=True)
     del fl, fo, fH, fws
 
+    # backward pass (gradients for upstream dO and dH_T) on the headline workload
+    bwd = time_backward(w, sets[0], torch, rsm, max(5, args.steps // 5))
+
+    # every other forward config
+    configs = {}
+    if not args.no_configs:
+        for name in ("tiny_f32", "long_t32768", "sweep_dense", "sweep_swa", "sweep_topk"):
+            configs[name] = time_forward_workload(name, torch, gen, rsm, 20 if name != "tiny_f32" else 200)
+    copy_bw = copy_bandwidth(torch)
+    print(f"[bench] device copy: {copy_bw['GB_per_s']:.0f} GB/s", file=sys.stderr, flush=True)
+
     rec = {
         "metric": METRIC,
         "value": tok / (ms_per_step * 1e-3),
@@ -335,14 +495,24 @@ def main():
                           "prefill_T": wd.T, "steps": args.decode_steps, "step_input_pool": n_pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "kernel": "rsm_forward_chunked call = fwd_scan_kernel pass A (routing its own segments, "
-                               "plus one route-only workgroup per head for the last segment) + fwd_scan_kernel "
-                               "pass B (two launches back to back on the caller's stream; the segment fold runs "
-                               "inside pass B at 4 segments)",
+                     "kernel": "rsm_forward_chunked call = seg_state_kernel (routes each segment and "
+                               "computes every segment state but the last's by the backward walk; one route-only "
+                               "workgroup per head routes the last segment) + fwd_scan_kernel pass B (two "
+                               "launches back to back on the caller's stream; the segment fold runs inside pass "
+                               "B at 4 segments)",
                      "algorithmic_bytes_per_launch": fbytes, "avg_launch_ms": kernel_ms},
         "decode_roofline": {"bound": "hbm", "achieved": dbytes / (dec_us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": dbytes / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                            "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes},
+                            "kernel": "decode_step_kernel", "algorithmic_bytes_per_launch": dbytes,
+                            "state_residency": "the 134 MB state fits in the 256 MB last-level cache across "
+                                               "steps; decode_rotated_states is the figure with the state "
+                                               "read from HBM"},
+        "decode_rotated_states": {"us_per_step": drot_us, "states": 3, "working_set_bytes": 3 * wd.B * wd.Hh *
+                                  wd.M * wd.Dv * 4, "achieved": dbytes / (drot_us * 1e-6) / 1e9, "unit": "GB/s",
+                                  "frac": dbytes / (drot_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
+        "backward": bwd,
+        "configs": configs,
+        "device_copy": copy_bw,
         "decode_default_layer": {"config": {"B": LB, "Hh": LHh, "M": LM, "Dv": LDv, "K": LK,
                                             "state": "random fp32", "step_input_pool": n_lpool},
                                  "us_per_step": dl_us, "algorithmic_bytes_per_launch": dl_bytes,

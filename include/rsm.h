@@ -182,6 +182,30 @@ int rsm_decode_step_ex(const void* q, const void* k, const void* z, const void* 
                        void* stream);
 
 /*
+ * Backward pass for training (the pages' chunked kernels exist for training: README kernel
+ * notes): the gradients of L = sum(dO * o) + sum(dH_T * H_out) for the default router, i.e.
+ * the vector-Jacobian product of rsm_forward_chunked with upstream gradients dO and dH_T.
+ *   q, k, z  [B,T,Hh,M]   dtype;  v [B,T,Hh,Dv] dtype;  f [B,T,Hh] fp32;  H0 [B,Hh,M,Dv] or NULL
+ *   dO       [B,T,Hh,Dv]  fp32 upstream gradient of o
+ *   dH_T     [B,Hh,M,Dv]  fp32 upstream gradient of the final state, or NULL (zero)
+ *   dq, dk, dz [B,T,Hh,M] fp32 out;  dv [B,T,Hh,Dv] fp32 out;  df [B,T,Hh] fp32 out
+ *   dH0      [B,Hh,M,Dv]  fp32 out, or NULL
+ *   workspace: at least rsm_backward_workspace_bytes() bytes (contents undefined)
+ * The top-K selection is piecewise constant in z: dz is nonzero only on the selected slots
+ * (through the sigmoid).  A full overwrite (f = -inf) gives no df or dz on that token.
+ * Outputs must not overlap any input or each other.  M in {16, 32, 64, 128, 256}, Dv in
+ * {16, ..., 256}.  The kernels walk each head's sequence token by token, its state split
+ * by slot groups (dq, dk, dz, df, dH0) or by column tiles (dv).
+ */
+size_t rsm_backward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M,
+                                    int64_t Dv, int64_t K);
+int rsm_backward(const void* q, const void* k, const void* z, const void* v, int dtype,
+                 const float* f, const float* H0, const float* dO, const float* dH_T, int64_t B,
+                 int64_t T, int64_t Hh, int64_t M, int64_t Dv, int64_t K, float* dq, float* dk,
+                 float* dz, float* dv, float* df, float* dH0, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
  * rsm_forward_chunked without a caller workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, results and errors as rsm_forward_chunked, whose kernels it

@@ -155,6 +155,46 @@ int rsm_forward_chunked_ex(const void* q, const void* k, const void* z, const vo
                                        static_cast<hipStream_t>(stream));
 }
 
+size_t rsm_backward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, int64_t M, int64_t Dv, int64_t K) {
+    if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv) || K < 1 || K > M) return 0;
+    const int64_t rows = mul_ck({B, T, Hh});
+    if (rows < 0 || mul_ck({rows, M, 16}) < 0) return 0;
+    return rsm::backward_workspace(long(B), long(T), long(Hh), int(M), int(K));
+}
+
+int rsm_backward(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
+                 const float* H0, const float* dO, const float* dH_T, int64_t B, int64_t T, int64_t Hh, int64_t M,
+                 int64_t Dv, int64_t K, float* dq, float* dk, float* dz, float* dv, float* df, float* dH0,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype)) return RSM_ERR_DTYPE;
+    if (B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv)) return RSM_ERR_SHAPE;
+    if (K < 1 || K > M) return RSM_ERR_K;
+    const int64_t rows = mul_ck({B, T, Hh});
+    const int64_t heads = mul_ck({B, Hh});
+    if (rows < 0 || heads < 0 || mul_ck({rows, M > Dv ? M : Dv, 16}) < 0) return RSM_ERR_SHAPE;
+    if (rows / 4 >= (int64_t(1) << 31) || heads * 16 >= (int64_t(1) << 31)) return RSM_ERR_SHAPE;
+    if (heads == 0) return RSM_OK;
+    if (T > 0 && (!q || !k || !z || !v || !f || !dO || !dq || !dk || !dz || !dv || !df)) return RSM_ERR_NULL;
+    const size_t need = rsm_backward_workspace_bytes(dtype, B, T, Hh, M, Dv, K);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return RSM_ERR_WORKSPACE;
+    const size_t es = esize(dtype);
+    const Range rq{q, size_t(rows * M) * es}, rk{k, size_t(rows * M) * es}, rz{z, size_t(rows * M) * es},
+        rv{v, size_t(rows * Dv) * es}, rf{f, size_t(rows) * 4}, rh0{H0, size_t(heads * M * Dv) * 4},
+        rdo{dO, size_t(rows * Dv) * 4}, rdh{dH_T, size_t(heads * M * Dv) * 4}, odq{dq, size_t(rows * M) * 4},
+        odk{dk, size_t(rows * M) * 4}, odz{dz, size_t(rows * M) * 4}, odv{dv, size_t(rows * Dv) * 4},
+        odf{df, size_t(rows) * 4}, odh{dH0, size_t(heads * M * Dv) * 4}, rw{workspace, need};
+    const Range ins[] = {rq, rk, rz, rv, rf, rh0, rdo, rdh};
+    const Range outs[] = {odq, odk, odz, odv, odf, odh, rw};
+    for (int a = 0; a < 7; ++a) {
+        for (const Range& b : ins)
+            if (overlap(outs[a], b)) return RSM_ERR_ALIAS;
+        for (int c = a + 1; c < 7; ++c)
+            if (overlap(outs[a], outs[c])) return RSM_ERR_ALIAS;
+    }
+    return rsm::backward_launch(q, k, z, v, dtype, f, H0, dO, dH_T, long(B), long(T), long(Hh), int(M), int(Dv),
+                                int(K), dq, dk, dz, dv, df, dH0, workspace, static_cast<hipStream_t>(stream));
+}
+
 int rsm_decode_step(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
                     float* H, int64_t B, int64_t Hh, int64_t M, int64_t Dv, int64_t K, float* o,
                     int32_t* idx_out, void* stream) {

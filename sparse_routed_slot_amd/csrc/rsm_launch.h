@@ -55,6 +55,14 @@ int forward_recurrent_launch(const void* q, const void* k, const void* z, const 
                              const float* H0, long B, long T, long Hh, int M, int Dv, int K, float* o, float* H_out,
                              int32_t* idx_out, void* workspace, const RouterOpts& op, hipStream_t stream);
 
+// Backward pass (default router): gradients of q, k, z, v, f and H0 for upstream gradients
+// dO and dH_T (nullable); workspace of backward_workspace() bytes.
+size_t backward_workspace(long B, long T, long Hh, int M, int K);
+int backward_launch(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
+                    const float* H0, const float* dO, const float* dHT, long B, long T, long Hh, int M, int Dv, int K,
+                    float* dq, float* dk, float* dz, float* dv, float* df, float* dH0, void* workspace,
+                    hipStream_t s);
+
 int forward_chunked_launch(const void* q, const void* k, const void* z, const void* v, int dtype,
                            const float* f, const float* H0, long B, long T, long Hh, int M,
                            int Dv, int K, int C, float* o, float* H_out, int32_t* idx_out,

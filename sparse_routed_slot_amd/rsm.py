@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["RSMError", "lib_path", "load", "route_topk", "forward_chunked", "forward_chunked_noalloc",
-           "noalloc_scratch_bytes", "decode_step",
+           "noalloc_scratch_bytes", "backward", "decode_step",
            "forward_workspace_bytes", "abi_version", "DTYPE_CODES", "SCORE_KINDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,11 @@ def load():
     lib.rsm_forward_chunked_ex.restype = I
     lib.rsm_decode_step_ex.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I64, P, P, O, P]
     lib.rsm_decode_step_ex.restype = I
+    lib.rsm_backward_workspace_bytes.argtypes = [I, I64, I64, I64, I64, I64, I64]
+    lib.rsm_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.rsm_backward.argtypes = [P, P, P, P, I, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P,
+                                 ctypes.c_size_t, P]
+    lib.rsm_backward.restype = I
     lib.rsm_noalloc_scratch_bytes.argtypes = []
     lib.rsm_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.rsm_forward_chunked_noalloc.argtypes = [P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I64, I64, P, P, P, P]
@@ -214,6 +219,36 @@ def forward_chunked_noalloc(q, k, z, v, f, K: int, C: int = 64, H0: Optional[tor
         _ptr(q), _ptr(k), _ptr(z), _ptr(v), _code(q), _ptr(f), _ptr(H0), B, T, Hh, M, Dv, K, C,
         _ptr(o), _ptr(H), _ptr(idx), _stream()))
     return o, H, idx
+
+
+def backward(q, k, z, v, f, K: int, dO, H0: Optional[torch.Tensor] = None, dHT: Optional[torch.Tensor] = None,
+             want_dH0: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Gradients of L = sum(dO * o) + sum(dHT * H_final) for the default router (the
+    vector-Jacobian product of forward_chunked).  dO fp32 [B,T,Hh,Dv]; dHT fp32 [B,Hh,M,Dv]
+    or None.  Returns (dq, dk, dz, dv, df, dH0 or None), all fp32."""
+    q, k, z, v, f, dO = (_dev(t, n) for t, n in zip((q, k, z, v, f, dO), ("q", "k", "z", "v", "f", "dO")))
+    if not (q.dtype == k.dtype == z.dtype == v.dtype) or f.dtype != torch.float32 or dO.dtype != torch.float32:
+        raise ValueError("q, k, z, v must share one dtype; f and dO must be float32")
+    B, T, Hh, M = q.shape
+    Dv = v.shape[-1]
+    if H0 is not None:
+        H0 = _dev(H0, "H0")
+    if dHT is not None:
+        dHT = _dev(dHT, "dHT")
+    dev = q.device
+    dq = torch.empty((B, T, Hh, M), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dz = torch.empty_like(dq)
+    dv = torch.empty((B, T, Hh, Dv), dtype=torch.float32, device=dev)
+    df = torch.empty((B, T, Hh), dtype=torch.float32, device=dev)
+    dH0 = torch.empty((B, Hh, M, Dv), dtype=torch.float32, device=dev) if want_dH0 else None
+    need = int(load().rsm_backward_workspace_bytes(_code(q), B, T, Hh, M, Dv, K))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(load().rsm_backward(_ptr(q), _ptr(k), _ptr(z), _ptr(v), _code(q), _ptr(f), _ptr(H0), _ptr(dO),
+                               _ptr(dHT), B, T, Hh, M, Dv, K, _ptr(dq), _ptr(dk), _ptr(dz), _ptr(dv), _ptr(df),
+                               _ptr(dH0), _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dz, dv, df, dH0
 
 
 def decode_step(q, k, z, v, f, H: torch.Tensor, K: int, want_idx: bool = False,
