@@ -307,6 +307,20 @@ __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* 
         }
         return;
     }
+    if (all) {  // K = M: every slot, in order, its logit from the row in registers
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const float s = sigmoidf_dev(x.val(i));
+            if (kFwd) {
+                alist[long(i) * C] = s > 0.0f ? __expf(s * ft) : 1.0f;
+                if (idx) idx[dst + i] = i;
+            } else {
+                idx[dst + i] = i;
+                if (score) score[dst + i] = s;
+            }
+        }
+        return;
+    }
     for (int n = 0; n < K; ++n) {
         int i;
         if (MW == 1 || m0 != 0ull) {

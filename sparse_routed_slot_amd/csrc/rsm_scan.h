@@ -359,13 +359,15 @@ __device__ __forceinline__ float scan_mul_step(float x) {
     const int y = __builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), CTRL, ROWMASK, 0xF, false);
     return x * __int_as_float(y);
 }
+// FULL = false: separate scans over lanes 0-31 and 32-63 (the row_bcast:31 step left out).
+template <bool FULL>
 __device__ __forceinline__ float wave_scan_mul(float x) {
     x = scan_mul_step<0x111, 0xF>(x);  // row_shr:1
     x = scan_mul_step<0x112, 0xF>(x);  // row_shr:2
     x = scan_mul_step<0x114, 0xF>(x);  // row_shr:4
     x = scan_mul_step<0x118, 0xF>(x);  // row_shr:8
     x = scan_mul_step<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = scan_mul_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    if constexpr (FULL) x = scan_mul_step<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -380,30 +382,47 @@ __device__ __forceinline__ float wave_scan_mul(float x) {
 #define RSM_STEPS4(CTRL) RSM_DPP4(CTRL, 0, 1, 2, 3)
 #define RSM_STEPS8(CTRL) RSM_STEPS4(CTRL) RSM_DPP4(CTRL, 4, 5, 6, 7)
 #define RSM_STEPS16(CTRL) RSM_STEPS8(CTRL) RSM_DPP4(CTRL, 8, 9, 10, 11) RSM_DPP4(CTRL, 12, 13, 14, 15)
-#define RSM_SCAN_ASM(STEPS)                                                                       \
+#define RSM_SCAN_ASM32(STEPS)                                                                     \
     "s_nop 1\n" STEPS("row_shr:1 row_mask:0xf") STEPS("row_shr:2 row_mask:0xf")                 \
         STEPS("row_shr:4 row_mask:0xf") STEPS("row_shr:8 row_mask:0xf")                          \
-            STEPS("row_bcast:15 row_mask:0xa") STEPS("row_bcast:31 row_mask:0xc")
-template <int N>
+            STEPS("row_bcast:15 row_mask:0xa")
+#define RSM_SCAN_ASM(STEPS) RSM_SCAN_ASM32(STEPS) STEPS("row_bcast:31 row_mask:0xc")
+// FULL = false: separate scans over lanes 0-31 and 32-63.
+template <int N, bool FULL = true>
 __device__ __forceinline__ void wave_scan_mul_n(float (&x)[N]) {
     static_assert(N == 2 || N == 4 || N == 8 || N == 16, "scan width");
     if constexpr (N == 2) {
-        x[0] = wave_scan_mul(x[0]);
-        x[1] = wave_scan_mul(x[1]);
+        x[0] = wave_scan_mul<FULL>(x[0]);
+        x[1] = wave_scan_mul<FULL>(x[1]);
     } else if constexpr (N == 4) {
-        asm volatile(RSM_SCAN_ASM(RSM_STEPS4) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+        if constexpr (FULL)
+            asm volatile(RSM_SCAN_ASM(RSM_STEPS4) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+        else
+            asm volatile(RSM_SCAN_ASM32(RSM_STEPS4) : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
     } else if constexpr (N == 8) {
-        asm volatile(RSM_SCAN_ASM(RSM_STEPS8)
-                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
-                       "+v"(x[7]));
+        if constexpr (FULL)
+            asm volatile(RSM_SCAN_ASM(RSM_STEPS8)
+                         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                           "+v"(x[7]));
+        else
+            asm volatile(RSM_SCAN_ASM32(RSM_STEPS8)
+                         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                           "+v"(x[7]));
     } else {
-        asm volatile(RSM_SCAN_ASM(RSM_STEPS16)
-                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
-                       "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
-                       "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+        if constexpr (FULL)
+            asm volatile(RSM_SCAN_ASM(RSM_STEPS16)
+                         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                           "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+                           "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+        else
+            asm volatile(RSM_SCAN_ASM32(RSM_STEPS16)
+                         : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                           "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]),
+                           "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
     }
 }
 #undef RSM_SCAN_ASM
+#undef RSM_SCAN_ASM32
 #undef RSM_STEPS16
 #undef RSM_STEPS8
 #undef RSM_STEPS4
@@ -443,7 +462,8 @@ __device__ __forceinline__ float clamp_alpha(float a) {
 //    waves, masked, and stored as ready-made MFMA fragments of P^T;
 //  Y: O^T = V^T P^T + H_c^T Qh^T for the wave's column tile (pass B), U = Kh^T V and the
 //    update H_{c+1} = diag(E_last)(H_c + U), and, independent of those, the decay products,
-//    Qh and Kh of chunk c+1 (lane = token, wave = group of SPW slots).
+//    Qh and Kh of chunk c+1 (lane = token, or two lanes per token with chunks of 32; wave =
+//    group of SPW slots).
 // Qh / Kh, the decay products, the alpha lists, the masks and the v tile are double-
 // buffered; the buffer is a compile-time index (even / odd chunk of the segment), so the
 // compiler can tell the direct global->LDS loads in flight from the other LDS accesses.
@@ -467,8 +487,13 @@ constexpr int tri_row(int s) {
 
 // Waves per workgroup: 16 for pass B with M <= 64 (8 state waves and 8 decay-product waves,
 // two of each per SIMD), else 8.
-template <bool PASS_A, int M>
+template <typename T, bool PASS_A, int M>
 constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
+// Wave roles split (state waves / decay-product waves) in pass B: M <= 64 (16 waves), and
+// bf16 M = 128 with chunks of 32 (8 waves: one of each kind per SIMD; 16 would not fit the
+// state and its split operands in 128 registers per wave).
+template <typename T, bool PASS_A, int M, int C>
+constexpr bool scan_split() { return !PASS_A && (M <= 64 || (M == 128 && C == 32 && sizeof(T) == 2)); }
 
 // FUSE (pass A only, bf16 inputs, default router, K <= 16, one Dv tile per head): the pass routes the
 // tokens itself -- each workgroup its own segment before the walk, and one extra workgroup
@@ -476,7 +501,7 @@ constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
 // the separate router kernel; z, f and idx_out are the router's inputs and optional output.
 // (rmask and ralpha carry no __restrict__: the fused pass writes the route through them.)
 template <typename T, int M, int C, int DT, bool PASS_A, bool FUSE>
-__global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kernel(
+__global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
     long T_len, int Hh, int Dv, int K, SegArgs sg, const unsigned long long* rmask,
     const float* ralpha, float* __restrict__ o, float* __restrict__ H_out, const T* __restrict__ z,
@@ -486,7 +511,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     typedef typename P::E E;
     typedef typename P::frag frag;
     typedef typename P::dfrag dfrag;
-    constexpr int NW = scan_waves<PASS_A, M>(), NT = 64 * NW;
+    constexpr int NW = scan_waves<T, PASS_A, M>(), NT = 64 * NW;
     constexpr int KB = P::KB, EPL = P::EPL, NPL = P::NPL;
     constexpr int MP = M > KB ? M : KB;        // padded slot dimension (k of slot contractions)
     constexpr int CP = C > KB ? C : KB;        // padded chunk dimension (k of row contractions)
@@ -496,11 +521,11 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     constexpr int EPG = 16 / int(sizeof(T));       // input elements per granule
     constexpr int NTC = C / 16, NTD = DT / 16, NTM = M / 16, NTMP = MP / 16;
     constexpr int NKM = MP / KB, NKC = CP / KB;
-    // Wave roles.  Pass B with M <= 64: the first half of the waves own the state columns
-    // (MFMA work), the second half compute the decay products; wave w runs on SIMD w % 4, so
-    // each SIMD runs both kinds and their vector and matrix work overlap.
+    // Wave roles.  Pass B with M <= 64 (and bf16 M = 128): the first half of the waves own
+    // the state columns (MFMA work), the second half compute the decay products; wave w runs
+    // on SIMD w % 4, so each SIMD runs both kinds and their vector and matrix work overlap.
     // Otherwise every wave does both.
-    constexpr bool SPLIT = !PASS_A && M <= 64;
+    constexpr bool SPLIT = scan_split<T, PASS_A, M, C>();
     constexpr int NMW = SPLIT ? NW / 2 : NW;         // state-column (MFMA) waves: 0 .. NMW-1
     constexpr int NPW = SPLIT ? NW / 2 : NW;         // decay-product waves: PW0 .. NW-1
     constexpr int PW0 = NW - NPW;
@@ -508,14 +533,18 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     constexpr int GT = NTD >= NMW ? 1 : NMW / NTD;   // MFMA waves per column tile
     constexpr int NTT = (NTC + GT - 1) / GT;         // output row tiles per MFMA wave, at most
     constexpr int SPW = M / NPW;                     // slots per decay-product wave
+    // lanes per token in the decay-product pass: with chunks of 32 a token's SPW slots are
+    // split between lanes t and t + 32 (every lane busy), else lane = token
+    constexpr int LPT = (C == 32 && SPW >= 4) ? 2 : 1;
+    constexpr int SPL = SPW / LPT;                   // slots per lane
     constexpr int MW = (M + 63) / 64;          // 64-bit words of a token's selection mask
     constexpr int NS = NTC * (NTC + 1) / 2;    // lower-triangular tiles of S^T
     constexpr int psQ = CP * QP + 8;           // plane stride of Qh / Kh
     constexpr int oK = NPL * psQ;              // Kh planes start here
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int psP = NTC * NKC * 64 * EPL;  // plane stride of the P^T fragments
-    constexpr int NWD = SPW * int(sizeof(T)) / 4;  // 32-bit words of a lane's q (or k) piece
-    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPW >= 2 && SPW <= 16 && C <= 64 && NMW <= 8,
+    constexpr int NWD = SPL * int(sizeof(T)) / 4;  // 32-bit words of a lane's q (or k) piece
+    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPL >= 2 && SPL <= 16 && C <= 64 && NMW <= 8,
                   "tile split");
     static_assert(2 * SZQK * int(sizeof(E)) >= 12 * C * M, "exact-path scratch");
 
@@ -578,7 +607,9 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     const int g = GT == 1 ? 0 : w / NTD;           // MFMA wave: token-tile group
     // column tile j of an MFMA wave
     auto Dj = [&](int j) { return GT == 1 ? w + NMW * j : w % NTD; };
-    const int s0 = (w - PW0) * SPW;                // decay-product wave: first slot
+    // decay-product lane: token tl of the chunk, slots s0 .. s0 + SPL - 1
+    const int tl = LPT == 1 ? lane : (lane & (C - 1));
+    const int s0 = (w - PW0) * SPW + (LPT == 1 ? 0 : (lane / C) * SPL);
     const long rstride = long(Hh);                  // rows between consecutive tokens of one head
     const long segrow = (bh * (sg.S - 1) + seg) * M;  // row of this segment in dH / dE
     auto valid_rows = [&](long c) { return int(T_len - c * C < C ? T_len - c * C : C); };
@@ -607,7 +638,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
                      [&](int off) { return static_cast<const void*>(mb + min(off, nm - 16)); });
     };
 
-    // ---- q and k pieces of the decay-product pass: lane = token, SPW slots from s0
+    // ---- q and k pieces of the decay-product pass: token tl, SPL slots from s0
     struct Seg {
         uint32_t wd[NWD];
     };
@@ -634,8 +665,8 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     auto load_qk = [&](long c, Seg& qs, Seg& ks) {
         // after every direct load of the phase: the waits for those skip these NQK loads
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const long t = c * C + lane;
-        const bool ok = lane < C && t < T_len;
+        const long t = c * C + tl;
+        const bool ok = tl < C && t < T_len;
         const long row = (ok ? t : 0) * rstride * M;
         Seg x, y;
         load_piece(kbase + row, x);
@@ -646,7 +677,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             qs.wd[p] = PASS_A ? 0u : ok ? y.wd[p] : 0u;
         }
     };
-    auto unpack = [&](const Seg& s, float (&x)[SPW]) {
+    auto unpack = [&](const Seg& s, float (&x)[SPL]) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int p = 0; p < NWD; ++p) {
@@ -659,12 +690,12 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         }
     };
 
-    // ---- the alphas of this lane's token for slots s0 .. s0+SPW-1: through the token's
+    // ---- the alphas of this lane's token for slots s0 .. s0+SPL-1: through the token's
     // selection mask (position in the alpha list = number of selected slots below); 1 for
     // unselected slots and for tokens past the sequence end.  A list position read for an
     // unselected slot may be past the list (stale LDS) and is discarded.
-    auto gather = [&](const float* rA, const unsigned long long* rM, int nvalid, float (&al)[SPW]) {
-        const int tc = lane < C ? lane : C - 1;
+    auto gather = [&](const float* rA, const unsigned long long* rM, int nvalid, float (&al)[SPL]) {
+        const int tc = tl < C ? tl : C - 1;
         unsigned long long word;
         int base;
         const unsigned long long w0 = rM[tc * MW];
@@ -675,11 +706,11 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             word = rM[tc * MW + 1];
             base = __popcll(w0) + __popcll(word & ((1ull << (s0 & 63)) - 1ull));
         }
-        if (lane >= nvalid) word = 0ull;
+        if (tl >= nvalid) word = 0ull;
         const uint32_t gsel = uint32_t(word >> (s0 & 63));
         int idx = base;
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
+        for (int j = 0; j < SPL; ++j) {
             const bool sel = (gsel >> j) & 1u;
             const float a = rA[idx * C + tc];
             al[j] = sel ? a : 1.0f;
@@ -693,11 +724,11 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
     // factored range.
     // pre(): called first (direct loads into buffers prep does not read); mid(): called once
     // the route of chunk c has been read (the direct loads go there)
-    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPW], auto&& pre, auto&& mid)
+    auto prep = [&](auto nb, long c, const Seg& qs, const Seg& ks, float (&Ev)[SPL], auto&& pre, auto&& mid)
                     __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
         E* sQK = NB ? sQK1 : sQK0;
-        float al[SPW];
+        float al[SPL];
         // q / k of this chunk are in: no later use of them has to wait behind the direct
         // loads issued next
         wait_vm<0>();
@@ -705,33 +736,34 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
         mid();
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) Ev[j] = clamp_alpha(al[j]);
-        wave_scan_mul_n<SPW>(Ev);
-        if (C == 64 || lane < C) {
-            float x[SPW];
+        for (int j = 0; j < SPL; ++j) Ev[j] = clamp_alpha(al[j]);
+        wave_scan_mul_n<SPL, LPT == 1>(Ev);
+        if (LPT == 2 || C == 64 || lane < C) {
+            float x[SPL];
             unpack(ks, x);
 #pragma unroll
-            for (int j = 0; j < SPW; ++j) x[j] = x[j] * (1.0f - clamp_alpha(al[j])) * __builtin_amdgcn_rcpf(Ev[j]);
-            P::template put_row<SPW>(sQK, psQ, oK + lane * QP + s0, x);
+            for (int j = 0; j < SPL; ++j) x[j] = x[j] * (1.0f - clamp_alpha(al[j])) * __builtin_amdgcn_rcpf(Ev[j]);
+            P::template put_row<SPL>(sQK, psQ, oK + tl * QP + s0, x);
             if (!PASS_A) {
                 unpack(qs, x);
 #pragma unroll
-                for (int j = 0; j < SPW; ++j) x[j] *= Ev[j];
-                P::template put_row<SPW>(sQK, psQ, lane * QP + s0, x);
+                for (int j = 0; j < SPL; ++j) x[j] *= Ev[j];
+                P::template put_row<SPL>(sQK, psQ, tl * QP + s0, x);
             }
         }
     };
-    // the last lane holds the decay products at the chunk end: store them, and the flag of
-    // one below the factored range
-    auto prep_tail = [&](auto nb, const float (&Ev)[SPW]) __attribute__((always_inline)) {
+    // the last lane of each token group (lane 63; lanes 31 and 63 with two lanes per token)
+    // holds the decay products at the chunk end: store them, and the wave's flag of one below
+    // the factored range
+    const bool tail_lane = LPT == 1 ? lane == 63 : tl == C - 1;
+    auto prep_tail = [&](auto nb, const float (&Ev)[SPL]) __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
-        if (lane == 63) {
-            Pol<float>::template put_row<SPW>(NB ? sE1 : sE0, 0, s0, Ev);
-            int bad = 0;
+        int bad = 0;
 #pragma unroll
-            for (int j = 0; j < SPW; ++j) bad |= !(Ev[j] >= kSafeMin);
-            (NB ? sF1 : sF0)[w] = bad;
-        }
+        for (int j = 0; j < SPL; ++j) bad |= !(Ev[j] >= kSafeMin);
+        const bool wbad = __builtin_amdgcn_ballot_w64(tail_lane && bad) != 0ull;
+        if (tail_lane) Pol<float>::template put_row<SPL>(NB ? sE1 : sE0, 0, s0, Ev);
+        if (lane == 63) (NB ? sF1 : sF0)[w] = wbad;
     };
 
     // ---- phase X: S^T tiles (J, TT), J <= TT, dealt to the state waves round-robin
@@ -742,17 +774,24 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             constexpr int S = decltype(sc)::value;
             constexpr int TT = tri_row(S), J = S - TT * (TT + 1) / 2;
             if (S % NMW == w) {
-                dfrag a[NKM], bq[NKM];
-#pragma unroll
-                for (int kb = 0; kb < NKM; ++kb)
-#pragma unroll
-                    for (int pl = 0; pl < NPL; ++pl) {
-                        a[kb].p[pl] = P::ld(sQK, oK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
-                        bq[kb].p[pl] = P::ld(sQK, pl * psQ + (16 * TT + l16) * QP + kb * KB + EPL * q4);
-                    }
+                // (with more than two k-blocks the fragments are loaded a pair of k-blocks at a
+                // time, so the state waves' registers hold the state besides them)
+                constexpr int KG = NKM > 2 ? 2 : NKM;
                 floatx4 st = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kb = 0; kb < NKM; ++kb) st = P::mm_dd(a[kb], bq[kb], st);
+                for (int k0 = 0; k0 < NKM; k0 += KG) {
+                    dfrag a[KG], bq[KG];
+#pragma unroll
+                    for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+                        for (int pl = 0; pl < NPL; ++pl) {
+                            const int kb = k0 + kk;
+                            a[kk].p[pl] = P::ld(sQK, oK + pl * psQ + (16 * J + l16) * QP + kb * KB + EPL * q4);
+                            bq[kk].p[pl] = P::ld(sQK, pl * psQ + (16 * TT + l16) * QP + kb * KB + EPL * q4);
+                        }
+#pragma unroll
+                    for (int kk = 0; kk < KG; ++kk) st = P::mm_dd(a[kk], bq[kk], st);
+                }
                 if (J == TT) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
@@ -796,11 +835,16 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             for (int kb = 0; kb < NKC; ++kb)
                 va[j][kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * Dj(j), kb, q4, l16);
         if (!PASS_A) {
-            dfrag hf[DPW][NKM];
+            // the state as hi / lo MFMA operands: split once when the wave has several output
+            // row tiles, else at its use, one k-block at a time (fewer live registers)
+            constexpr bool HPRE = NTT > 1;
+            dfrag hf[HPRE ? DPW : 1][HPRE ? NKM : 1];
+            if constexpr (HPRE) {
 #pragma unroll
-            for (int j = 0; j < DPW; ++j)
+                for (int j = 0; j < DPW; ++j)
 #pragma unroll
-                for (int kb = 0; kb < NKM; ++kb) hf[j][kb] = P::pack_perm(Hreg[j], kb);
+                    for (int kb = 0; kb < NKM; ++kb) hf[j][kb] = P::pack_perm(Hreg[j], kb);
+            }
             // outputs go out by buffer stores whose offset is out of range for rows past the
             // sequence end (dropped by the hardware), so no branch splits this block
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -809,11 +853,15 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
                 constexpr int N = decltype(nc)::value, TT = G + GT * N;
                 if constexpr (TT < NTC) {
                     dfrag qf[NKM], pf[NKC];  // shared by the wave's column tiles
-#pragma unroll
-                    for (int kb = 0; kb < NKM; ++kb)
+                    auto load_qf = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
                         for (int pl = 0; pl < NPL; ++pl)
                             qf[kb].p[pl] = P::ld_jrow(sQK, pl * psQ + (16 * TT + l16) * QP, kb, q4);
+                    };
+                    if constexpr (HPRE) {
+#pragma unroll
+                        for (int kb = 0; kb < NKM; ++kb) load_qf(kb);
+                    }
 #pragma unroll
                     for (int kb = 0; kb < NKC; ++kb)
                         if (kb * KB < 16 * (TT + 1)) pf[kb] = P::template ld_pfrag<NKC>(sP, psP, TT, kb, lane);
@@ -825,7 +873,14 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
                         for (int kb = 0; kb < NKC; ++kb)
                             if (kb * KB < 16 * (TT + 1)) acc = P::mm_vd(va[j][kb], pf[kb], acc);
 #pragma unroll
-                        for (int kb = 0; kb < NKM; ++kb) acc = P::mm_dd(hf[j][kb], qf[kb], acc);
+                        for (int kb = 0; kb < NKM; ++kb) {
+                            if constexpr (HPRE) {
+                                acc = P::mm_dd(hf[j][kb], qf[kb], acc);
+                            } else {
+                                if (j == 0) load_qf(kb);
+                                acc = P::mm_dd(P::pack_perm(Hreg[j], kb), qf[kb], acc);
+                            }
+                        }
                         const int off =
                             tl < nvalid ? int((tl * rstride * Dv + 16 * Dj(j) + 4 * q4) * 4) : kOutRange + 16;
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32x4, acc), orsrc, off, 0, 0);
@@ -867,23 +922,23 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         float* sE = CUR ? sE1 : sE0;
         const T* rvc = CUR ? rv1 : rv0;
         if constexpr (DP) {
-            float al[SPW], x[SPW];
+            float al[SPL], x[SPL];
             gather(CUR ? rA1 : rA0, CUR ? rM1 : rM0, nvalid, al);
             Seg qs2, ks2;
             load_qk(c, qs2, ks2);
-            if (C == 64 || lane < C) {
-                Pol<float>::template put_row<SPW>(xa, 0, lane * M + s0, al);
+            if (LPT == 2 || C == 64 || lane < C) {
+                Pol<float>::template put_row<SPL>(xa, 0, tl * M + s0, al);
                 unpack(ks2, x);
-                Pol<float>::template put_row<SPW>(xk, 0, lane * M + s0, x);
+                Pol<float>::template put_row<SPL>(xk, 0, tl * M + s0, x);
                 if (!PASS_A) {
                     unpack(qs2, x);
-                    Pol<float>::template put_row<SPW>(xa, 0, C * M + lane * M + s0, x);
+                    Pol<float>::template put_row<SPL>(xa, 0, C * M + tl * M + s0, x);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < SPW; ++j) x[j] = al[j];
-            wave_scan_mul_n<SPW>(x);  // exact decay products
-            if (lane == 63) Pol<float>::template put_row<SPW>(sE, 0, s0, x);
+            for (int j = 0; j < SPL; ++j) x[j] = al[j];
+            wave_scan_mul_n<SPL, LPT == 1>(x);  // exact decay products
+            if (tail_lane) Pol<float>::template put_row<SPL>(sE, 0, s0, x);
         }
         wg_barrier();
         if constexpr (DM) {
@@ -910,6 +965,9 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
                             part = fmaf(x4.z, Hreg[j][I][2], part);
                             part = fmaf(x4.w, Hreg[j][I][3], part);
                         }
+                        // a slot tile at a time: the loads of the next are not hoisted above
+                        // this one (the wave's registers are mostly state)
+                        if constexpr (NTM > 4) __builtin_amdgcn_sched_barrier(0);
                     }
                     if (!PASS_A) {
                         part += __shfl_xor(part, 16);
@@ -959,7 +1017,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
         auto issue_route_next = [&]() {
             if (c + 2 < c_end) issue_route(c + 2, CUR ? rA1 : rA0, CUR ? rM1 : rM0);
         };
-        float Ev[SPW];
+        float Ev[SPL];
         if (unsafe) {
             exact(cur, c, nvalid, dm, dp);
             if (MP > M || CP > C) {
@@ -1027,7 +1085,30 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             // segments per batch of loads: all of them if their (E, dH) values fit in about 144
             // registers, else one at a time
             constexpr int FB = NTM * (1 + DPW) * 4 * kFoldMax <= (NW > 8 ? 64 : 144) ? kFoldMax : 1;
+            // (with one segment per batch, one slot tile at a time, the scheduler kept from
+            // hoisting the loads of the next: a wave whose registers are mostly state)
+            constexpr bool TILEWISE = FB == 1 && NTM > 4;
             for (int s0 = 0; seg > 0 && !folded && s0 < seg; s0 += FB) {
+                if constexpr (TILEWISE) {
+                    const long sr = (bh * (sg.S - 1) + s0) * M;
+                    static_for<NTM>([&](auto ic) {
+                        constexpr int I = decltype(ic)::value;
+                        float ev[4], xv[DPW][4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            ev[r] = sg.dE[sr + 16 * I + 4 * q4 + r];
+#pragma unroll
+                            for (int j = 0; j < DPW; ++j) xv[j][r] = sg.dH[sr * Dv + at(j, I, r)];
+                        }
+#pragma unroll
+                        for (int j = 0; j < DPW; ++j)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)  // untouched rows keep their bits
+                                Hreg[j][I][r] = ev[r] != 1.0f ? fmaf(ev[r], Hreg[j][I][r], xv[j][r]) : Hreg[j][I][r];
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    continue;
+                }
                 float ev[FB][NTM][4], xv[FB][DPW][NTM][4];
 #pragma unroll
                 for (int sj = 0; sj < FB; ++sj) {
@@ -1061,7 +1142,7 @@ __global__ __launch_bounds__((64 * scan_waves<PASS_A, M>())) void fwd_scan_kerne
             __builtin_amdgcn_s_waitcnt(0);
             wg_barrier();  // the loads and the zero fill are done
             if constexpr (DP) {
-                float Ev[SPW];
+                float Ev[SPL];
                 prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev, [] {}, [] {});
                 prep_tail(std::integral_constant<int, 0>{}, Ev);
             }
@@ -1127,14 +1208,14 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
             }
             if (fuse && !routed) {  // pass A routes: one more workgroup per head for the last segment
                 hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, true>),
-                                   dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<true, M>()), 0,
+                                   dim3(unsigned(tiles * (sg.S - 1) + B * Hh)), dim3(64 * scan_waves<T, true, M>()), 0,
                                    s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
                 routed = true;
             }
         }
         if (!routed)
             hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false>), dim3(unsigned(tiles * (sg.S - 1))),
-                               dim3(64 * scan_waves<true, M>()), 0, s,
+                               dim3(64 * scan_waves<T, true, M>()), 0, s,
                                q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
         if (sg.S > kFoldMax + 1) {
@@ -1143,7 +1224,7 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
         }
     }
     hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false, false>), dim3(unsigned(tiles * sg.S)),
-                       dim3(64 * scan_waves<false, M>()), 0, s, q, k, v,
+                       dim3(64 * scan_waves<T, false, M>()), 0, s, q, k, v,
                        H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
