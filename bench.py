@@ -455,7 +455,7 @@ def main():
     print(f"[bench] decode, default layer shape (B{LB} Hh{LHh} M{LM} Dv{LDv} K{LK}): {dl_us:.2f} us/step, "
           f"{dl_bytes / (dl_us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # forward at the pages' default layer shape (M = 256: the recurrent form)
+    # forward at the pages' default layer shape (M = 256, bf16, K = 32: chunked, chunks of 32)
     FB, FT, FHh, FM, FDv, FK = 16, 2048, 4, 256, 256, 32
     fl = to_dev(gen.make_inputs(FB, FT, FHh, FM, FDv, "bf16", 11), torch)
     fo = torch.empty((FB, FT, FHh, FDv), dtype=torch.float32, device="cuda")
@@ -476,7 +476,7 @@ def main():
     torch.cuda.synchronize()
     fl_us = e0.elapsed_time(e1) * 1e3 / n_fl
     fl_bytes = forward_bytes(FB, FT, FHh, FM, FDv, 2)
-    print(f"[bench] forward, default layer shape (B{FB} T{FT} Hh{FHh} M{FM} Dv{FDv} K{FK}, recurrent form): "
+    print(f"[bench] forward, default layer shape (B{FB} T{FT} Hh{FHh} M{FM} Dv{FDv} K{FK}, chunked): "
           f"{fl_us:.0f} us/call, {FB * FT / fl_us:.2f} M tok/s", file=sys.stderr, flush=True)
     del fl, fo, fH, fws
 
@@ -536,8 +536,8 @@ def main():
                                  "achieved": dl_bytes / (dl_us * 1e-6) / 1e9, "unit": "GB/s",
                                  "frac": dl_bytes / (dl_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
         "forward_default_layer": {"config": {"B": FB, "T": FT, "Hh": FHh, "M": FM, "Dv": FDv, "K": FK,
-                                             "form": "recurrent (router over all rows, then one workgroup per "
-                                                     "head and column tile walks the tokens)"},
+                                             "form": "chunked: the chunk router, then the chunk scan with chunks "
+                                                     "of 32 and 64-column tiles (one segment)"},
                                   "us_per_call": fl_us, "tokens_per_s": FB * FT / (fl_us * 1e-6),
                                   "algorithmic_bytes_per_launch": fl_bytes,
                                   "achieved": fl_bytes / (fl_us * 1e-6) / 1e9, "unit": "GB/s",

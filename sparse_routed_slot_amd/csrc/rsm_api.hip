@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "rsm_launch.h"
+#include "rsm_scan_args.h"
 
 namespace {
 
@@ -102,8 +103,12 @@ size_t rsm_forward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh, 
     if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv) || !c_ok(C)) return 0;
     if (K < 1 || K > M) return 0;
     if (mul_ck({B, T + C, Hh, M, 5}) < 0 || mul_ck({B, Hh, T / C + 2, M, Dv, 4}) < 0) return 0;
-    if (M == 256) return rsm::forward_recurrent_workspace(long(B), long(T), long(Hh), int(K));
-    return rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C), int(K)).total;
+    const size_t chunked = rsm::forward_layout(dtype, long(B), long(T), long(Hh), int(M), int(Dv), int(C), int(K)).total;
+    if (M != 256) return chunked;
+    // M = 256: the recurrent form's workspace, or the chunked one (bf16, K <= 32: the default
+    // router runs chunked, a variant recurrent), whichever is larger
+    const size_t rec = rsm::forward_recurrent_workspace(long(B), long(T), long(Hh), int(K));
+    return (dtype == RSM_BF16 && K <= rsm::kRouteKCap256 && chunked > rec) ? chunked : rec;
 }
 
 int rsm_forward_chunked(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,

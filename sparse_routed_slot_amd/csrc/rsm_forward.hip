@@ -64,15 +64,22 @@ int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Chunk length the kernels run: the requested C, except M = 128, whose C = 64 tiles do not
-// fit in LDS and run as chunks of 32 (same result up to rounding).
-static int scan_chunk(int M, int C) { return (M == 128 && C > 32) ? 32 : C; }
+// fit in LDS and run as chunks of 32, and M = 256, which always runs chunks of 32 (same
+// result up to rounding).
+static int scan_chunk(int M, int C) { return M == 256 ? 32 : (M == 128 && C > 32) ? 32 : C; }
 
 // Dv tile of a workgroup: the whole head up to 128 columns (bf16) / 64 (fp32), half that
-// for M = 128, so the fp32 state tile is at most 32 KB.
+// for M >= 128 (the fp32 state tile is at most 32 KB, 64 KB at M = 256).
 static int pick_dt(int dtype, int M, int Dv) {
     int cap = dtype == RSM_F32 ? 64 : 128;
     if (M >= 128) cap /= 2;
     return Dv < cap ? Dv : cap;
+}
+
+// M = 256 runs chunked for bf16 inputs with the default router and K <= 32 (the alpha lists
+// in LDS are sized for that), else in the recurrent form.
+bool chunked_m256(int dtype, int K, const RouterOpts& op) {
+    return dtype == RSM_BF16 && op.is_default() && K <= kRouteKCap256;
 }
 
 // Enough workgroups to fill the chip: segments per head so that heads x Dv tiles x
@@ -119,6 +126,7 @@ static int dispatch_m(int dtype, int M, int C, int DT, const ScanArgs& a) {
         case 32: return f ? scan_f32_m32(C, DT, a) : scan_bf16_m32(C, DT, a);
         case 64: return f ? scan_f32_m64(C, DT, a) : scan_bf16_m64(C, DT, a);
         case 128: return f ? scan_f32_m128(C, DT, a) : scan_bf16_m128(C, DT, a);
+        case 256: return f ? RSM_ERR_UNSUPPORTED : scan_bf16_m256(C, DT, a);
     }
     return RSM_ERR_UNSUPPORTED;
 }
@@ -135,7 +143,7 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
         hipLaunchKernelGGL(copy_state_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, H0, H_out, n);
         return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
     }
-    if (M == 256)  // chunk tiles of 256 slots do not fit in LDS: the recurrent form
+    if (M == 256 && !chunked_m256(dtype, K, op))  // the recurrent form
         return forward_recurrent_launch(q, k, z, v, dtype, f, H0, B, T, Hh, M, Dv, K, o, H_out, idx_out, workspace, op,
                                         stream);
     const FwdLayout L = forward_layout(dtype, B, T, Hh, M, Dv, C, K);
@@ -153,7 +161,7 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
                      reinterpret_cast<float*>(ws + L.de_off)};
     // With more than one segment and one Dv tile per head the first pass routes its own
     // segments (bf16 inputs, default router, K <= 16); otherwise the router kernel runs first.
-    const bool fuse = dtype == RSM_BF16 && op.is_default() && K <= 16 && L.S > 1 && L.dt == Dv;
+    const bool fuse = dtype == RSM_BF16 && op.is_default() && K <= 16 && L.S > 1 && L.dt == Dv && M <= 128;
     if (!fuse) {
         const int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.chunk, idx_out, rmask,
                                         ralpha, op, stream);

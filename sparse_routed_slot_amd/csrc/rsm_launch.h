@@ -43,6 +43,8 @@ struct FwdLayout {
     int cps;    // chunks per segment
 };
 FwdLayout forward_layout(int dtype, long B, long T, long Hh, int M, int Dv, int C, int K);
+// whether the forward at M = 256 runs chunked (else in the recurrent form)
+bool chunked_m256(int dtype, int K, const RouterOpts& op);
 
 int route_fwd_launch(const void* z, int dtype, const float* f, long B, long T, long Hh, long T_pad, int M, int K,
                      int C, int32_t* idx_out, unsigned long long* rmask, float* ralpha, const RouterOpts& op,

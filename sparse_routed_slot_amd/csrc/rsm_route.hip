@@ -17,6 +17,7 @@
 #include "rsm_device.h"
 #include "rsm_launch.h"
 #include "rsm_route_row.h"
+#include "rsm_scan_args.h"
 
 namespace rsm {
 
@@ -257,6 +258,60 @@ __global__ __launch_bounds__(256) void route_wave_kernel(const T* __restrict__ z
         }
 }
 
+// Forward router at M = 256 (default router), for the chunked forward: one workgroup of 8
+// waves per (b*Hh + h, chunk of C tokens).  Wave w routes tokens w, w + 8, ... of the chunk,
+// a token per wave (lane l holds slots r*64 + l, the exact top-K by the bitwise threshold
+// search of wave_topk), alpha = exp(s*f) of each selected slot going to its list position.
+// The chunk's alpha lists (slot-major: entry n of token t at n*C + t) and selection masks
+// (token-major, 4 words per token) are assembled in LDS and written out contiguously, so
+// every store is coalesced; entries of tokens past the sequence end are never read.
+template <typename T>
+__global__ __launch_bounds__(512) void route_chunk_wave_kernel(const T* __restrict__ z, const float* __restrict__ f,
+                                                               long T_len, int Hh, long T_pad, int K, int C,
+                                                               int32_t* __restrict__ idx,
+                                                               unsigned long long* __restrict__ rmask,
+                                                               float* __restrict__ ralpha) {
+    constexpr int M = 256, SPL = M / kWave, MW = M / 64, NWV = 8;
+    constexpr int NB = Elem<T>::kKeyBits;
+    __shared__ float sA[kRouteKCap256 * 64];          // [n][C], C <= 64
+    __shared__ unsigned long long sM[64 * MW];         // [t][MW]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const long nch = T_pad / C;
+    const long bh = long(blockIdx.x) / nch, c = long(blockIdx.x) % nch;
+    const long hb = bh / Hh, hh = bh % Hh;
+    for (int tt = w; tt < C; tt += NWV) {
+        const long t = c * C + tt;
+        if (t >= T_len) break;  // the whole wave
+        const long row = (hb * T_len + t) * Hh + hh;
+        float zv[SPL];
+        uint32_t key[SPL];
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            zv[r] = Elem<T>::load(z + row * M, r * kWave + lane);
+            key[r] = order_key<NB>(zv[r]);
+        }
+        const float ft = f[row];
+        bool sel[SPL];
+        wave_topk<SPL, NB>(key, K, sel);
+        int pos[SPL];
+        wave_compact<SPL>(sel, pos);
+#pragma unroll
+        for (int r = 0; r < SPL; ++r) {
+            const unsigned long long m = __ballot(sel[r]);
+            if (lane == 0) sM[tt * MW + r] = m;
+            if (sel[r]) {
+                const float sc = sigmoidf_dev(zv[r]);
+                sA[pos[r] * C + tt] = sc > 0.0f ? __expf(sc * ft) : 1.0f;
+                if (idx) idx[row * K + pos[r]] = r * kWave + lane;
+            }
+        }
+    }
+    __syncthreads();
+    const long tok0 = bh * T_pad + c * C;
+    for (int i = threadIdx.x; i < K * C; i += NWV * kWave) ralpha[tok0 * K + i] = sA[i];
+    for (int i = threadIdx.x; i < C * MW; i += NWV * kWave) rmask[tok0 * MW + i] = sM[i];
+}
+
 template <typename T, bool kFwd>
 static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int Hh, long T_pad, int M, int K, int C,
                        int32_t* idx, float* score, unsigned long long* rmask, float* ralpha, const RouterOpts& op,
@@ -266,8 +321,14 @@ static int launch_rows(const T* z, const float* f, long n_rows, long T_len, int 
     const dim3 grid(static_cast<unsigned>(nblk)), block(64);
     const size_t lds = 0;
     const bool ex = !op.is_default();
-    if (M == 256) {  // public router only (the chunked forward takes M <= 128)
-        if (kFwd) return RSM_ERR_UNSUPPORTED;
+    if (M == 256) {
+        if (kFwd) {  // the chunked forward's route (default router, K <= 32, chunks of at most 64)
+            if (ex || K > kRouteKCap256 || C > 64 || T_pad % C != 0) return RSM_ERR_UNSUPPORTED;
+            const long nblk_c = (n_rows / T_len) * (T_pad / C);
+            hipLaunchKernelGGL((route_chunk_wave_kernel<T>), dim3(static_cast<unsigned>(nblk_c)), dim3(512), 0,
+                               stream, z, f, T_len, Hh, T_pad, K, C, idx, rmask, ralpha);
+            return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
+        }
         const dim3 g4(static_cast<unsigned>((n_rows + 3) / 4)), b4(256);
         if (ex)
             hipLaunchKernelGGL((route_wave_kernel<T, 256, true>), g4, b4, 0, stream, z, n_rows, K, idx, score, op);

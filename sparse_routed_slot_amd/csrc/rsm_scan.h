@@ -390,8 +390,11 @@ __device__ __forceinline__ float wave_scan_mul(float x) {
 // FULL = false: separate scans over lanes 0-31 and 32-63.
 template <int N, bool FULL = true>
 __device__ __forceinline__ void wave_scan_mul_n(float (&x)[N]) {
-    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "scan width");
-    if constexpr (N == 2) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "scan width");
+    if constexpr (N == 32) {  // two blocks of 16 independent values
+        wave_scan_mul_n<16, FULL>(*reinterpret_cast<float(*)[16]>(&x[0]));
+        wave_scan_mul_n<16, FULL>(*reinterpret_cast<float(*)[16]>(&x[16]));
+    } else if constexpr (N == 2) {
         x[0] = wave_scan_mul<FULL>(x[0]);
         x[1] = wave_scan_mul<FULL>(x[1]);
     } else if constexpr (N == 4) {
@@ -490,10 +493,14 @@ constexpr int tri_row(int s) {
 template <typename T, bool PASS_A, int M>
 constexpr int scan_waves() { return (!PASS_A && M <= 64) ? 16 : 8; }
 // Wave roles split (state waves / decay-product waves) in pass B: M <= 64 (16 waves), and
-// bf16 M = 128 with chunks of 32 (8 waves: one of each kind per SIMD; 16 would not fit the
-// state and its split operands in 128 registers per wave).
+// bf16 M = 128 and 256 with chunks of 32 (8 waves: one of each kind per SIMD; 16 would not
+// fit the state and its split operands in 128 registers per wave).
 template <typename T, bool PASS_A, int M, int C>
-constexpr bool scan_split() { return !PASS_A && (M <= 64 || (M == 128 && C == 32 && sizeof(T) == 2)); }
+constexpr bool scan_split() { return !PASS_A && (M <= 64 || (M >= 128 && C == 32 && sizeof(T) == 2)); }
+// Alpha-list entries per token the LDS route buffers hold: K <= M up to 128 slots, K <= 32 at
+// M = 256 (the host takes the token-by-token form beyond that).
+template <int M>
+constexpr int route_kcap() { return M <= 128 ? M : kRouteKCap256; }
 
 // FUSE (pass A only, bf16 inputs, default router, K <= 16, one Dv tile per head): the pass routes the
 // tokens itself -- each workgroup its own segment before the walk, and one extra workgroup
@@ -544,16 +551,17 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     constexpr int SZQK = 2 * NPL * psQ;
     constexpr int psP = NTC * NKC * 64 * EPL;  // plane stride of the P^T fragments
     constexpr int NWD = SPL * int(sizeof(T)) / 4;  // 32-bit words of a lane's q (or k) piece
-    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPL >= 2 && SPL <= 16 && C <= 64 && NMW <= 8,
+    static_assert((NMW % NTD == 0 || NTD % NMW == 0) && SPL >= 2 && SPL <= 32 && C <= 64 && NMW <= 8,
                   "tile split");
+    constexpr int KCAP = route_kcap<M>();
     static_assert(2 * SZQK * int(sizeof(E)) >= 12 * C * M, "exact-path scratch");
 
     // LDS.  Every array is a separate object so the compiler can tell the direct loads from
-    // the other accesses.  Route arrays are sized for K = M.
+    // the other accesses.  Route arrays are sized for K = KCAP.
     __shared__ __align__(16) T rv0[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, even chunks
     __shared__ __align__(16) T rv1[pad1k(CP * DT * int(sizeof(T))) / int(sizeof(T))];  // v, odd chunks
-    __shared__ __align__(16) float rA0[pad1k(C * M * 4) / 4];  // alpha lists, slot-major
-    __shared__ __align__(16) float rA1[pad1k(C * M * 4) / 4];
+    __shared__ __align__(16) float rA0[pad1k(C * KCAP * 4) / 4];  // alpha lists, slot-major
+    __shared__ __align__(16) float rA1[pad1k(C * KCAP * 4) / 4];
     __shared__ __align__(16) unsigned long long rM0[pad1k(C * MW * 8) / 8];  // selection masks
     __shared__ __align__(16) unsigned long long rM1[pad1k(C * MW * 8) / 8];
     __shared__ __align__(16) E sQK0[SZQK];  // Qh planes, then Kh planes
@@ -570,7 +578,7 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     const int nseg = PASS_A ? sg.S - 1 : sg.S;
     long nblk = gridDim.x;
     // routing segment sgi of head bhr: one token per thread, rows past the sequence end skipped
-    auto route_segment = [&](long bhr, long sgi) {
+    auto route_segment = [&](auto bhr, long sgi) {  // (generic: instantiated only where FUSE calls it)
         const long t_lo = sgi * sg.cps * C;
         const long t_end = (sgi + 1) * sg.cps * C;
         const long t_hi = t_end < T_len ? t_end : T_len;
@@ -696,16 +704,13 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     // unselected slot may be past the list (stale LDS) and is discarded.
     auto gather = [&](const float* rA, const unsigned long long* rM, int nvalid, float (&al)[SPL]) {
         const int tc = tl < C ? tl : C - 1;
-        unsigned long long word;
-        int base;
-        const unsigned long long w0 = rM[tc * MW];
-        if (MW == 1 || s0 < 64) {
-            word = w0;
-            base = __popcll(w0 & ((1ull << (s0 & 63)) - 1ull));
-        } else {
-            word = rM[tc * MW + 1];
-            base = __popcll(w0) + __popcll(word & ((1ull << (s0 & 63)) - 1ull));
-        }
+        // the mask word holding slots s0 .. s0+SPL-1 (SPL <= 32 slots never straddle two),
+        // and the selected slots in the words below it
+        const int wi = s0 >> 6;
+        unsigned long long word = rM[tc * MW + wi];
+        int base = __popcll(word & ((1ull << (s0 & 63)) - 1ull));
+#pragma unroll
+        for (int j = 0; j + 1 < MW; ++j) base += j < wi ? __popcll(rM[tc * MW + j]) : 0;
         if (tl >= nvalid) word = 0ull;
         const uint32_t gsel = uint32_t(word >> (s0 & 63));
         int idx = base;
@@ -834,7 +839,60 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 va[j][kb] = P::template ld_col_swz<true, GV, 2>(rvc, 0, 16 * Dj(j), kb, q4, l16);
-        if (!PASS_A) {
+        // more than four k-blocks of slots (M = 256): k-block outer, the state split one
+        // k-block at a time and applied to every output row tile (few live registers, the
+        // accumulators of the row tiles independent)
+        constexpr bool KOUTER = NKM > 4;
+        if constexpr (!PASS_A && KOUTER) {
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                o + ((b * T_len + c * C) * rstride + h) * Dv + d0, short(0), kOutRange, kBufferFlags);
+            floatx4 acc[NTT][DPW];
+            static_for<NTT>([&](auto nc) {
+                constexpr int N = decltype(nc)::value, TT = G + GT * N;
+#pragma unroll
+                for (int j = 0; j < DPW; ++j) acc[N][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (TT < NTC) {
+#pragma unroll
+                    for (int kb = 0; kb < NKC; ++kb)
+                        if (kb * KB < 16 * (TT + 1)) {
+                            const dfrag pf = P::template ld_pfrag<NKC>(sP, psP, TT, kb, lane);
+#pragma unroll
+                            for (int j = 0; j < DPW; ++j) acc[N][j] = P::mm_vd(va[j][kb], pf, acc[N][j]);
+                        }
+                }
+            });
+#pragma unroll
+            for (int kb = 0; kb < NKM; ++kb) {
+                dfrag hk[DPW];
+#pragma unroll
+                for (int j = 0; j < DPW; ++j) hk[j] = P::pack_perm(Hreg[j], kb);
+                static_for<NTT>([&](auto nc) {
+                    constexpr int N = decltype(nc)::value, TT = G + GT * N;
+                    if constexpr (TT < NTC) {
+                        dfrag qk;
+#pragma unroll
+                        for (int pl = 0; pl < NPL; ++pl)
+                            qk.p[pl] = P::ld_jrow(sQK, pl * psQ + (16 * TT + l16) * QP, kb, q4);
+#pragma unroll
+                        for (int j = 0; j < DPW; ++j) acc[N][j] = P::mm_dd(hk[j], qk, acc[N][j]);
+                    }
+                });
+            }
+            static_for<NTT>([&](auto nc) {
+                constexpr int N = decltype(nc)::value, TT = G + GT * N;
+                if constexpr (TT < NTC) {
+                    const int tl = 16 * TT + l16;
+#pragma unroll
+                    for (int j = 0; j < DPW; ++j) {
+                        const int off =
+                            tl < nvalid ? int((tl * rstride * Dv + 16 * Dj(j) + 4 * q4) * 4) : kOutRange + 16;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint32x4, acc[N][j]), orsrc, off, 0,
+                                                               0);
+                    }
+                }
+            });
+        }
+        if (!PASS_A && !KOUTER) {
             // the state as hi / lo MFMA operands: split once when the wave has several output
             // row tiles, else at its use, one k-block at a time (fewer live registers)
             constexpr bool HPRE = NTT > 1;
@@ -907,6 +965,9 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
                 for (int r = 0; r < 4; ++r)  // rows of slots untouched in the chunk (E = 1) keep their bits
                     Hreg[j][I][r] = ev[r] < 1.0f ? ev[r] * (Hreg[j][I][r] + u[r]) : Hreg[j][I][r];
             }
+            // (M = 256: two slot tiles at a time, so the loads of the others are not hoisted
+            // into the registers the state already fills)
+            if constexpr (NTM > 8 && I % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         });
     };
 
@@ -1071,7 +1132,10 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
             // place of dH_{s-1} between the two passes; otherwise it is folded here, every
             // segment's (E, dH) loaded at once.
             auto at = [&](int j, int I, int r) { return (16 * I + 4 * q4 + r) * Dv + d0 + 16 * Dj(j) + l16; };
-            const bool folded = sg.S > kFoldMax + 1;
+            // (M = 256: always folded by the fold kernel; the in-kernel fold's loads would not
+            // fit beside the state)
+            constexpr bool kFoldHere = M <= 128;
+            const bool folded = sg.S > kFoldMax + 1 || !kFoldHere;
             const float* hs = (seg > 0 && folded) ? sg.dH + (bh * (sg.S - 1) + seg - 1) * M * Dv
                                                   : H0 ? H0 + bh * M * Dv : nullptr;
             if (hs) {
@@ -1088,7 +1152,7 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
             // (with one segment per batch, one slot tile at a time, the scheduler kept from
             // hoisting the loads of the next: a wave whose registers are mostly state)
             constexpr bool TILEWISE = FB == 1 && NTM > 4;
-            for (int s0 = 0; seg > 0 && !folded && s0 < seg; s0 += FB) {
+            for (int s0 = 0; kFoldHere && seg > 0 && !folded && s0 < seg; s0 += FB) {
                 if constexpr (TILEWISE) {
                     const long sr = (bh * (sg.S - 1) + s0) * M;
                     static_for<NTM>([&](auto ic) {
@@ -1195,7 +1259,7 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
     const T* z = static_cast<const T*>(zr);
     if (sg.S > 1) {
         bool routed = false;
-        if constexpr (std::is_same<T, bf16_t>::value) {  // fp32 rows would spill in the pass
+        if constexpr (std::is_same<T, bf16_t>::value && M <= 128) {  // fp32 rows would spill in the pass
             if constexpr (C >= 32) {
                 if (fuse) {  // segment states by the backward walk, which routes: one more workgroup
                              // per head routes the last segment
@@ -1218,7 +1282,7 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
                                dim3(64 * scan_waves<T, true, M>()), 0, s,
                                q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
         if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
-        if (sg.S > kFoldMax + 1) {
+        if (sg.S > kFoldMax + 1 || M > 128) {
             const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);
             if (st != RSM_OK) return st;
         }
@@ -1236,7 +1300,7 @@ static int dispatch_dt(int DT, const ScanArgs& a) {
 #define RSM_SCAN(DTV) \
     return launch_scan<T, M, C, DTV>(q, k, v, a.H0, a.B, a.T_len, a.Hh, a.Dv, a.K, a.sg, a.rmask, a.ralpha, a.o, \
                                      a.H_out, a.z, a.f, a.idx_out, a.fuse_route, a.s)
-    constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);
+    constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);  // (M = 256: 64, bf16 only)
     switch (DT) {
         case 16: RSM_SCAN(16);
         case 32: RSM_SCAN(32);
@@ -1253,14 +1317,18 @@ static int dispatch_dt(int DT, const ScanArgs& a) {
 
 template <typename T, int M>
 static int dispatch_c(int C, int DT, const ScanArgs& a) {
-    switch (C) {
-        case 16: return dispatch_dt<T, M, 16>(DT, a);
-        case 32: return dispatch_dt<T, M, 32>(DT, a);
-        case 64:
-            if constexpr (M < 128) return dispatch_dt<T, M, 64>(DT, a);
-            break;
+    if constexpr (M == 256) {  // bf16, chunks of 32 only
+        return C == 32 ? dispatch_dt<T, M, 32>(DT, a) : RSM_ERR_UNSUPPORTED;
+    } else {
+        switch (C) {
+            case 16: return dispatch_dt<T, M, 16>(DT, a);
+            case 32: return dispatch_dt<T, M, 32>(DT, a);
+            case 64:
+                if constexpr (M < 128) return dispatch_dt<T, M, 64>(DT, a);
+                break;
+        }
+        return RSM_ERR_UNSUPPORTED;
     }
-    return RSM_ERR_UNSUPPORTED;
 }
 
 }  // namespace rsm

@@ -8,6 +8,9 @@
 
 namespace rsm {
 
+// Largest K of the chunked forward at M = 256 (the alpha lists in LDS are sized for it).
+constexpr int kRouteKCap256 = 32;
+
 struct SegArgs {
     long nC;    // chunks in the sequence
     int S;      // segments
@@ -51,6 +54,7 @@ RSM_SCAN_DECL(bf16, 16)
 RSM_SCAN_DECL(bf16, 32)
 RSM_SCAN_DECL(bf16, 64)
 RSM_SCAN_DECL(bf16, 128)
+RSM_SCAN_DECL(bf16, 256)
 #undef RSM_SCAN_DECL
 
 }  // namespace rsm

@@ -111,9 +111,15 @@ def test_workspace_size(lib):
     # enough heads for the whole chip: one segment, the route only
     assert f(1, 64, 2048, 8, 64, 128, 64, 16) < 64 * 2048 * 8 * (8 + 16 * 4) + 4096
     assert f(0, 1, 2048, 8, 64, 128, 64, 16) >= 1 * 2048 * 8 * (8 + 16 * 4)
-    # M = 256 (recurrent form): the router's K indices and K weights per token-head
+    # M = 256, recurrent form (fp32, a router variant, or K > 32): the router's K indices and
+    # K weights per token-head, each part 256-byte aligned
+    assert f(0, 16, 2048, 4, 256, 256, 64, 32) == 2 * 16 * 2048 * 4 * 32 * 4
+    assert f(0, 1, 3, 1, 256, 64, 64, 5) == 2 * 256
+    assert f(1, 1, 3, 1, 256, 64, 64, 40) == 2 * 512
+    # bf16 with K <= 32: the larger of that and the chunked route (chunks of 32 tokens: four
+    # mask words and K decay factors per padded token-head)
     assert f(1, 16, 2048, 4, 256, 256, 64, 32) == 2 * 16 * 2048 * 4 * 32 * 4
-    assert f(1, 1, 3, 1, 256, 64, 64, 5) == 2 * 256                  # each part 256-byte aligned
+    assert f(1, 1, 3, 1, 256, 64, 64, 5) == 32 * 4 * 8 + 768      # 640 bytes of factors, aligned
     assert f(1, 1, 0, 1, 256, 64, 64, 5) == 0
 
 

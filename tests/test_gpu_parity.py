@@ -482,13 +482,20 @@ def test_variant_route_wide_rows(rsm, var, dtype):
     np.testing.assert_allclose(sc.cpu().numpy(), rsc, rtol=2e-5, atol=1e-7)
 
 
-# ------------------------------------------------ forward at M = 256 (recurrent form)
+# ------------------------------------------------ forward at M = 256
+# bf16 with K <= 32 runs chunked (chunks of 32, 64-column tiles); fp32 and K > 32 run in the
+# recurrent form.
 M256_CASES = [  # dtype, B, T, Hh, Dv, K, h0, f = -inf tokens
     ("bf16", 2, 70, 2, 64, 32, False, False),
-    ("bf16", 1, 150, 2, 256, 32, True, True),    # four column tiles, T not a multiple of 4
-    ("f32", 1, 33, 1, 16, 100, True, False),     # K > 64: several route entries per lane
-    ("f32", 1, 5, 3, 32, 256, False, False),     # K = M: every slot every token
+    ("bf16", 1, 150, 2, 256, 32, True, True),    # four column tiles, segments, exact chunks
+    ("f32", 1, 33, 1, 16, 100, True, False),     # recurrent: K > 64, several route entries per lane
+    ("f32", 1, 5, 3, 32, 256, False, False),     # recurrent: K = M, every slot every token
     ("bf16", 3, 1, 2, 128, 8, True, False),      # one token
+    ("bf16", 2, 130, 2, 32, 16, True, True),     # 32-column tile (two state waves per column tile)
+    ("bf16", 1, 64, 3, 16, 1, False, False),     # 16-column tile, top-1
+    ("bf16", 4, 96, 4, 128, 32, True, False),    # two column tiles, two segments
+    ("bf16", 16, 100, 4, 256, 32, False, False), # 256 tiles: one segment
+    ("bf16", 1, 97, 1, 64, 40, True, False),     # recurrent: K > 32
 ]
 
 
@@ -507,6 +514,17 @@ def test_forward_m256(rsm, case):
             for h in range(Hh):
                 never[b, h, np.unique(idx[b, :, h, :])] = False
         assert np.array_equal(H[never], d["H0"][never])
+
+
+def test_forward_default_layer_sampled(rsm):
+    """The pages' default layer at its bench size (B16 T2048 Hh4 M256 d_v256 K32, chunked):
+    indices, outputs and final states of sequences 0 and 15 against the oracle."""
+    B, T, Hh, M, Dv, K = 16, 2048, 4, 256, 256, 32
+    log(f"forward default layer B{B} T{T} Hh{Hh} M{M} Dv{Dv} K{K}")
+    d = gen.make_inputs(B, T, Hh, M, Dv, "bf16", 11)
+    o, H, idx = run_forward(rsm, d, K, 64)
+    for b in (0, B - 1):
+        compare_forward(d, K, o, H, idx, sl=slice(b, b + 1), what=f"default layer b={b}")
 
 
 def test_forward_m256_inplace_and_empty(rsm):
