@@ -120,32 +120,40 @@ __device__ __forceinline__ void pk_select(const uint32_t (&raw)[M / 2], int K, u
     u16x2 key[M / 2];
 #pragma unroll
     for (int r = 0; r < M / 2; ++r) key[r] = pair_keys(raw[r]);
-    u16x2 e[16];
-    {
-        u16x2 w[NB][16];
+    unsigned short th;
+    if (K == 1) {  // the largest key: a running maximum, no network
+        u16x2 mx = key[0];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int r = 1; r < M / 2; ++r) mx = __builtin_elementwise_max(mx, key[r]);
+        th = mx.x > mx.y ? mx.x : mx.y;
+    } else {
+        u16x2 e[16];
+        {
+            u16x2 w[NB][16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) w[b][i] = key[16 * b + i];
-            pk_sort16_desc(w[b]);
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) w[b][i] = key[16 * b + i];
+                pk_sort16_desc(w[b]);
+            }
+            if constexpr (NB == 1) {
+                pk_combine(w[0], w[0], e);
+            } else if constexpr (NB == 2) {
+                u16x2 q[16];
+                pk_combine(w[0], w[1], q);
+                pk_combine(q, q, e);
+            } else {
+                u16x2 q0[16], q1[16], r[16];
+                pk_combine(w[0], w[1], q0);
+                pk_combine(w[2], w[3], q1);
+                pk_combine(q0, q1, r);
+                pk_combine(r, r, e);
+            }
         }
-        if constexpr (NB == 1) {
-            pk_combine(w[0], w[0], e);
-        } else if constexpr (NB == 2) {
-            u16x2 q[16];
-            pk_combine(w[0], w[1], q);
-            pk_combine(q, q, e);
-        } else {
-            u16x2 q0[16], q1[16], r[16];
-            pk_combine(w[0], w[1], q0);
-            pk_combine(w[2], w[3], q1);
-            pk_combine(q0, q1, r);
-            pk_combine(r, r, e);
-        }
+        th = e[0].x;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) th = (r == K - 1) ? e[r].x : th;
     }
-    unsigned short th = e[0].x;
-#pragma unroll
-    for (int r = 1; r < 16; ++r) th = (r == K - 1) ? e[r].x : th;
     pk_mask_ge<M>(key, th, mk);
     int cnt = 0;
 #pragma unroll
