@@ -164,7 +164,7 @@ size_t rsm_backward_workspace_bytes(int dtype, int64_t B, int64_t T, int64_t Hh,
     if (!dtype_ok(dtype) || B < 0 || T < 0 || Hh < 0 || !m_ok_rd(M) || !dv_ok(Dv) || K < 1 || K > M) return 0;
     const int64_t rows = mul_ck({B, T, Hh});
     if (rows < 0 || mul_ck({rows, M, 16}) < 0) return 0;
-    return rsm::backward_workspace(long(B), long(T), long(Hh), int(M), int(K));
+    return rsm::backward_workspace(long(B), long(T), long(Hh), int(M), int(Dv), int(K));
 }
 
 int rsm_backward(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,

@@ -15,8 +15,10 @@ __global__ void copy_state_kernel(const float* __restrict__ H0, float* __restric
 
 // Segment fold (see seg_fold_launch): one thread per 4 consecutive columns of a state row;
 // the segments are walked in order, their (E, dH) read a batch at a time ahead of use.
+// keep: a row whose product E is 1 (untouched in the segment, so its dH is zero) keeps its
+// bits; otherwise every row is folded.
 __global__ void seg_fold_kernel(const float* __restrict__ H0, float* __restrict__ dH, const float* __restrict__ dE,
-                                long n4, int S, int M, int Dv) {
+                                long n4, int S, int M, int Dv, int keep) {
     constexpr int NB = 8;
     for (long idx = long(blockIdx.x) * blockDim.x + threadIdx.x; idx < n4; idx += long(gridDim.x) * blockDim.x) {
         const long e0 = idx * 4;
@@ -40,7 +42,7 @@ __global__ void seg_fold_kernel(const float* __restrict__ H0, float* __restrict_
             for (int j = 0; j < NB; ++j) {
                 if (s0 + j < S - 1) {
                     const long r = (bh * (S - 1) + s0 + j) * M + i;
-                    if (e[j] != 1.0f)  // rows untouched in the segment keep their bits
+                    if (!keep || e[j] != 1.0f)  // rows untouched in the segment keep their bits
                         hv = make_float4(fmaf(e[j], hv.x, x[j].x), fmaf(e[j], hv.y, x[j].y), fmaf(e[j], hv.z, x[j].z),
                                          fmaf(e[j], hv.w, x[j].w));
                     *reinterpret_cast<float4*>(dH + r * Dv + d) = hv;
@@ -50,11 +52,11 @@ __global__ void seg_fold_kernel(const float* __restrict__ H0, float* __restrict_
     }
 }
 
-int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream) {
+int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream, bool keep) {
     const long n4 = BH * M * Dv / 4;
     const long blocks = (n4 + 255) / 256;
     hipLaunchKernelGGL(seg_fold_kernel, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, H0, sg.dH,
-                       sg.dE, n4, sg.S, M, Dv);
+                       sg.dE, n4, sg.S, M, Dv, keep ? 1 : 0);
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 

@@ -59,7 +59,7 @@ int forward_recurrent_launch(const void* q, const void* k, const void* z, const 
 
 // Backward pass (default router): gradients of q, k, z, v, f and H0 for upstream gradients
 // dO and dH_T (nullable); workspace of backward_workspace() bytes.
-size_t backward_workspace(long B, long T, long Hh, int M, int K);
+size_t backward_workspace(long B, long T, long Hh, int M, int Dv, int K);
 int backward_launch(const void* q, const void* k, const void* z, const void* v, int dtype, const float* f,
                     const float* H0, const float* dO, const float* dHT, long B, long T, long Hh, int M, int Dv, int K,
                     float* dq, float* dk, float* dz, float* dv, float* df, float* dH0, void* workspace,

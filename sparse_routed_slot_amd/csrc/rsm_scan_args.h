@@ -40,7 +40,9 @@ struct ScanArgs {
 
 // Between the two passes: dH_s <- H_start(s+1) = diag(E_s) H_start(s) + dH_s for s = 0 .. S-2,
 // H_start(0) = H0 (or zero), so that each segment of pass B reads its start state directly.
-int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream);
+// keep: rows with E_s = 1 keep their bits (their dH_s is zero); false for a fold whose
+// untouched rows still carry a contribution (the backward's gradient carries).
+int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream, bool keep = true);
 
 // Launch passes A (if S > 1) and B of the chunk scan for one input type and slot count M;
 // C and DT are the chunk length and Dv tile the layout chose.  Each is defined in its own

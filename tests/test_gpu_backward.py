@@ -67,6 +67,8 @@ def run_and_compare(rsm, d, K, dO, dHT, what, sl=None):
     log(f"{what}: " + ", ".join(msg))
 
 
+# The passes cut each head's tokens into up to S segments (T / S >= 64, about 2048 workgroups):
+# T = 256 at M = 16 runs 4, T = 130 runs 2, T <= 100 runs one.
 SMALL = [  # dtype, B, T, Hh, M, Dv, K, H0, dHT, f=-inf tokens
     ("f32", 1, 256, 2, 16, 16, 4, False, False, False),
     ("f32", 2, 100, 3, 64, 128, 16, True, True, False),
@@ -76,6 +78,10 @@ SMALL = [  # dtype, B, T, Hh, M, Dv, K, H0, dHT, f=-inf tokens
     ("f32", 1, 60, 2, 128, 32, 128, True, False, False),
     ("bf16", 1, 40, 2, 256, 256, 32, True, True, False),
     ("bf16", 3, 1, 2, 64, 128, 16, True, True, False),
+    # sequence segments walked in parallel (4 of 76, 76, 76, 73 tokens; 2 of 100 at M = 256)
+    ("bf16", 1, 301, 3, 32, 32, 8, True, True, True),
+    ("bf16", 1, 200, 1, 256, 64, 32, True, True, False),
+    ("f32", 2, 512, 1, 16, 64, 16, False, True, False),
 ]
 
 
