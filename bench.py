@@ -33,6 +33,8 @@ COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 FWD_SOURCES = ["rsm_forward.hip", "rsm_route.hip", "rsm_route_row.h", "rsm_scan.h", "rsm_scan_args.h",
                "rsm_segstate.h", "rsm_scan_bf16_m64.hip", "rsm_device.h", "rsm_launch.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "forward_fwd_b8_t2048_traffic.txt")
+# the forward configs besides the headline one (timed once each; parity cases in the tests)
+CONFIG_NAMES = ("tiny_f32", "long_t32768", "sweep_dense", "sweep_swa", "sweep_topk")
 
 
 def forward_bytes(B, T, Hh, M, Dv, es):
@@ -256,6 +258,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the timing of the other forward configs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="time only the other forward configs and print their records (for profiling them "
+                         "apart from the headline workload); not the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -272,6 +277,12 @@ def main():
         build.build_library()
     rsm.load()
     torch.cuda.set_device(0)
+
+    if args.only_configs:
+        out = {name: time_forward_workload(name, torch, gen, rsm, 20 if name != "tiny_f32" else 200)
+               for name in CONFIG_NAMES}
+        print(json.dumps({"configs": out}), flush=True)
+        return
 
     # ---------------------------------------------------------------- forward
     w = gen.WORKLOADS["fwd_b8_t2048"]
@@ -486,7 +497,7 @@ def main():
     # every other forward config
     configs = {}
     if not args.no_configs:
-        for name in ("tiny_f32", "long_t32768", "sweep_dense", "sweep_swa", "sweep_topk"):
+        for name in CONFIG_NAMES:
             configs[name] = time_forward_workload(name, torch, gen, rsm, 20 if name != "tiny_f32" else 200)
     copy_bw = copy_bandwidth(torch)
     print(f"[bench] device copy: {copy_bw['GB_per_s']:.0f} GB/s", file=sys.stderr, flush=True)

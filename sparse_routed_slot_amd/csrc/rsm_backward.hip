@@ -150,12 +150,13 @@ __global__ __launch_bounds__(256) void bwd_rows_fwd_kernel(const T* __restrict__
     float pa[kPF], pk[kPF], pv[kPF][CG], pd[kPF][CG];
     auto load = [&](int j, long t) __attribute__((always_inline)) {
         const long row = r0 + (t < tb ? t : tb - 1) * Hh;  // past the segment: a valid row, unused
-        pa[j] = a_d[row * M + i];
-        pk[j] = ld(k, row * M + i);
+        // (row pointers are uniform over the block: scalar base + 32-bit lane offset)
+        pa[j] = (a_d + row * M)[i];
+        pk[j] = ld(k + row * M, i);
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-            pv[j][c] = ld(v, row * Dv + cg * CG + c);
-            if (!PRE) pd[j][c] = dO[row * Dv + cg * CG + c];
+            pv[j][c] = ld(v + row * Dv, cg * CG + c);
+            if (!PRE) pd[j][c] = (dO + row * Dv)[cg * CG + c];
         }
     };
 #pragma unroll
@@ -169,15 +170,16 @@ __global__ __launch_bounds__(256) void bwd_rows_fwd_kernel(const T* __restrict__
                 float p = 0.0f;
 #pragma unroll
                 for (int c = 0; c < CG; ++c) {
-                    // unselected rows (a == 1) keep their bits
-                    H[c] = a != 1.0f ? fmaf(a, H[c], kw * pv[j][c]) : H[c];
+                    // (an unselected row, a = 1 and kw = 0, keeps its value; the state here only
+                    // feeds gradients, so no select for the sign of a zero)
+                    H[c] = fmaf(a, H[c], kw * pv[j][c]);
                     if (!PRE) p = fmaf(pd[j][c], H[c], p);
                 }
                 if (PRE) {
                     E *= a;
                 } else {
                     p = row16_sum(p);
-                    if (cg == 0) dq[(r0 + t * Hh) * M + i] = p;
+                    if (cg == 0) (dq + (r0 + t * Hh) * M)[i] = p;
                 }
             }
             load(j, t + kPF);
@@ -203,6 +205,10 @@ __global__ __launch_bounds__(256) void bwd_rows_fwd_kernel(const T* __restrict__
 // Pass 3: rows backward (layout of pass 2) -> dk, dz, dg s, dH0.  PRE: segments 1 .. S-1 from
 // a zero carry, their local carries and alpha products into Gs / Ps (slot S-1-s); else every
 // segment from its carry (dH_T, or the folded Gs) with the outputs.
+// (the rows-backward pass keeps four tokens of loads in flight: with eight its many
+// per-token scalars spill scalar registers)
+constexpr int kPFR = 4;
+
 template <typename T, int CG, bool PRE>
 __global__ __launch_bounds__(256) void bwd_rows_rev_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const float* __restrict__ f,
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(256) void bwd_rows_rev_kernel(const T* __restrict__
         for (int c = 0; c < CG; ++c) G[c] = 0.0f;
     }
     float E = 1.0f;
-    float pq[kPF], pk[kPF], pa[kPF], ps[kPF], pdq[kPF], pf[kPF], pv[kPF][CG], pd[kPF][CG];
+    float pq[kPFR], pk[kPFR], pa[kPFR], ps[kPFR], pdq[kPFR], pf[kPFR], pv[kPFR][CG], pd[kPFR][CG];
     auto load = [&](int j, long t) __attribute__((always_inline)) {
         const long row = r0 + (t >= ta ? t : ta) * Hh;
         pq[j] = ld(q, row * M + i);
@@ -260,9 +266,9 @@ __global__ __launch_bounds__(256) void bwd_rows_rev_kernel(const T* __restrict__
         }
     };
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) load(j, tb - 1 - j);
-    for (long t0 = tb - 1; t0 >= ta; t0 -= kPF) {
-        unroll<kPF>([&](auto jc) __attribute__((always_inline)) {
+    for (int j = 0; j < kPFR; ++j) load(j, tb - 1 - j);
+    for (long t0 = tb - 1; t0 >= ta; t0 -= kPFR) {
+        unroll<kPFR>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
             const long t = t0 - j;
             if (t >= ta) {
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(256) void bwd_rows_rev_kernel(const T* __restrict__
 #pragma unroll
                 for (int c = 0; c < CG; ++c) G[c] *= a;
             }
-            load(j, t - kPF);
+            load(j, t - kPFR);
         });
     }
     if (PRE) {
@@ -337,13 +343,13 @@ __global__ __launch_bounds__(256) void bwd_cols_rev_kernel(const T* __restrict__
     float pdo[kPF], pq[kPF][SPT], pw[kPF][SPT], pa[kPF][SPT];
     auto load = [&](int j, long t) __attribute__((always_inline)) {
         const long row = r0 + (t >= ta ? t : ta) * Hh;
-        pdo[j] = dO[row * Dv + c];
+        pdo[j] = (dO + row * Dv)[c];
 #pragma unroll
         for (int x = 0; x < SPT; ++x) {
             const int i = sg * SPT + x;
-            pq[j][x] = ld(q, row * M + i);
-            pa[j][x] = a_d[row * M + i];
-            pw[j][x] = (1.0f - pa[j][x]) * ld(k, row * M + i);
+            pq[j][x] = ld(q + row * M, i);
+            pa[j][x] = (a_d + row * M)[i];
+            pw[j][x] = (1.0f - pa[j][x]) * ld(k + row * M, i);
         }
     };
 #pragma unroll
@@ -411,9 +417,9 @@ __global__ __launch_bounds__(256) void bwd_cols_lane_kernel(const T* __restrict_
         for (int e = threadIdx.x; e < nb * M; e += 256) {
             const int tt = e / M, x = e % M;
             const long row = r0 + (t0 + tt) * Hh;
-            const float a = a_d[row * M + x];
-            sQ[e] = ld(q, row * M + x);
-            sW[e] = (1.0f - a) * ld(k, row * M + x);
+            const float a = (a_d + row * M)[x];
+            sQ[e] = ld(q + row * M, x);
+            sW[e] = (1.0f - a) * ld(k + row * M, x);
             sA[e] = a;
         }
         float d[TB];
