@@ -1263,10 +1263,20 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
             if constexpr (C >= 32) {
                 if (fuse) {  // segment states by the backward walk, which routes: one more workgroup
                              // per head routes the last segment
-                    hipLaunchKernelGGL((seg_state_kernel<M, C, DT>), dim3(unsigned(B * Hh * sg.S)), dim3(512), 0, s,
-                                       reinterpret_cast<const bf16_t*>(k), reinterpret_cast<const bf16_t*>(v),
-                                       reinterpret_cast<const bf16_t*>(z), f, T_len, int(Hh), Dv, K, sg,
-                                       const_cast<unsigned long long*>(rmask), const_cast<float*>(ralpha), idx_out);
+                    // M = 128, a segment that fits one routing round: the variant without mid-walk
+                    // rounds (whose routing beside the walk's live registers spills there; at M <= 64
+                    // it measured slower than the round-by-round kernel)
+                    if (M >= 128 && long(sg.cps) * C <= seg_round_one<M, C, DT>())
+                        hipLaunchKernelGGL((seg_state_kernel<M, C, DT, true>), dim3(unsigned(B * Hh * sg.S)), dim3(512),
+                                           0, s, reinterpret_cast<const bf16_t*>(k), reinterpret_cast<const bf16_t*>(v),
+                                           reinterpret_cast<const bf16_t*>(z), f, T_len, int(Hh), Dv, K, sg,
+                                           const_cast<unsigned long long*>(rmask), const_cast<float*>(ralpha), idx_out);
+                    else
+                        hipLaunchKernelGGL((seg_state_kernel<M, C, DT, false>), dim3(unsigned(B * Hh * sg.S)),
+                                           dim3(512), 0, s, reinterpret_cast<const bf16_t*>(k),
+                                           reinterpret_cast<const bf16_t*>(v), reinterpret_cast<const bf16_t*>(z), f,
+                                           T_len, int(Hh), Dv, K, sg, const_cast<unsigned long long*>(rmask),
+                                           const_cast<float*>(ralpha), idx_out);
                     routed = true;
                 }
             }

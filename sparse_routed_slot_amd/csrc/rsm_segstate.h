@@ -24,7 +24,23 @@
 // running product.
 namespace rsm {
 
+// LDS of seg_state_kernel besides the route of a round, and the largest round (a multiple of
+// the 512 threads) that fits beside it in 160 KB: a segment no longer than that is routed in
+// one round before its walk (no routing while the walk's registers are live).
 template <int M, int C, int DT>
+constexpr int seg_lds_base() {
+    constexpr int MP = M > 32 ? M : 32, QP = MP + 8, psW = C * QP + 8;
+    constexpr int SPL = M > 64 ? M / 64 : 1;
+    return 2 * 2 * psW * 2 + 4 * ((C * DT * 2 + 1023) / 1024 * 1024) + 2 * 8 * 64 * SPL * 4;
+}
+template <int M, int C, int DT>
+constexpr int seg_round_one() {
+    constexpr int per_tok = ((M + 63) / 64) * 8 + 16 * 4;  // mask words and 16 alpha-list entries
+    constexpr int r = (160 * 1024 - seg_lds_base<M, C, DT>()) / per_tok / 512 * 512;
+    return r > 512 ? r : 512;
+}
+
+template <int M, int C, int DT, bool ONE>
 __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                         const bf16_t* __restrict__ z, const float* __restrict__ f,
                                                         long T_len, int Hh, int Dv, int K, SegArgs sg,
@@ -42,7 +58,7 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     constexpr int SPL = M > 64 ? M / 64 : 1;  // slots per lane
     constexpr int MW = (M + 63) / 64;         // mask words per token
     constexpr int TPW = C / NW;               // tokens per wave in a chunk
-    constexpr int R = NT;                     // tokens per routing round
+    constexpr int R = ONE ? seg_round_one<M, C, DT>() : NT;  // tokens per routing round
     constexpr int NTM = M / 16, NTD = DT / 16, NKC = C / KB;
     constexpr int NOT = NTM * NTD;             // 16x16 output tiles of U
     constexpr int NPT = (NOT + NW - 1) / NW;   // output tiles per wave, at most
@@ -127,10 +143,10 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     long rl0 = 0;
     auto route_round = [&](long lo, long n) __attribute__((always_inline)) {
         rl0 = lo;
-        if (tid < n) {
-            const long t = lo + tid;
+        for (int tr = tid; tr < n; tr += NT) {
+            const long t = lo + tr;
             route_row<bf16_t, M, true, true, true>(z, f, rowbase + t * rstride, bh, t, T_pad, K, C, idx_out, nullptr,
-                                                   rmask, ralpha, sMask + tid * MW, sList + tid * K);
+                                                   rmask, ralpha, sMask + tr * MW, sList + tr * K);
         }
         wait_vm<0>();
         __syncthreads();
@@ -270,7 +286,8 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     auto step = [&](auto ph, long s) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;  // s % 4
         const long c = c_last - s;
-        if (s > 0 && s < nsteps && c * C + C == rl0) route_round(round_lo(c), rl0 - round_lo(c));  // next round
+        if constexpr (!ONE)
+            if (s > 0 && s < nsteps && c * C + C == rl0) route_round(round_lo(c), rl0 - round_lo(c));  // next round
         const long cv = c > c_first ? c : c_first, ck = c - 1 > c_first ? c - 1 : c_first;
         constexpr int PV = (PH + 2) & 3;
         issue_v(cv, PV == 0 ? rv0 : PV == 1 ? rv1 : PV == 2 ? rv2 : rv3);
