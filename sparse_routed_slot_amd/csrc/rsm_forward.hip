@@ -52,6 +52,12 @@ __global__ void seg_fold_kernel(const float* __restrict__ H0, float* __restrict_
     }
 }
 
+// idx of a dense route (K = M): slot i in entry i of every token-head row
+__global__ void idx_iota_kernel(int32_t* __restrict__ idx, long n, int M) {
+    const long e = long(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (e < n) idx[e] = int32_t(e % M);
+}
+
 int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream, bool keep) {
     const long n4 = BH * M * Dv / 4;
     const long blocks = (n4 + 255) / 256;
@@ -164,12 +170,19 @@ int forward_chunked_launch(const void* q, const void* k, const void* z, const vo
     // With more than one segment and one Dv tile per head the first pass routes its own
     // segments (bf16 inputs, default router, K <= 16); otherwise the router kernel runs first.
     const bool fuse = dtype == RSM_BF16 && op.is_default() && K <= 16 && L.S > 1 && L.dt == Dv && M <= 128;
-    if (!fuse) {
+    const bool dense = dtype == RSM_BF16 && op.is_default() && K == M && M == 128;
+    if (dense) {
+        if (idx_out) {
+            const long n = B * T * Hh * long(M);
+            hipLaunchKernelGGL(idx_iota_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, idx_out, n, M);
+            if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
+        }
+    } else if (!fuse) {
         const int st = route_fwd_launch(z, dtype, f, B, T, Hh, L.n_chunks * L.chunk, M, K, L.chunk, idx_out, rmask,
                                         ralpha, op, stream);
         if (st != RSM_OK) return st;
     }
-    const ScanArgs a{q, k, v, H0, B, T, Hh, Dv, K, sg, rmask, ralpha, o, H_out, stream, z, f, idx_out, fuse};
+    const ScanArgs a{q, k, v, H0, B, T, Hh, Dv, K, sg, rmask, ralpha, o, H_out, stream, z, f, idx_out, fuse, dense};
     return dispatch_m(dtype, M, L.chunk, L.dt, a);
 }
 

@@ -507,13 +507,17 @@ constexpr int route_kcap() { return M <= 128 ? M : kRouteKCap256; }
 // per head (past the scan's grid) the last segment, which pass B alone reads -- in place of
 // the separate router kernel; z, f and idx_out are the router's inputs and optional output.
 // (rmask and ralpha carry no __restrict__: the fused pass writes the route through them.)
-template <typename T, int M, int C, int DT, bool PASS_A, bool FUSE>
+// DENSE (K = M with the default router: every slot selected every token): no route in memory;
+// the decay-product waves form alpha = exp(sigmoid(z) f) from z and f themselves, loaded
+// beside k (the router's formula, so the same alphas).
+template <typename T, int M, int C, int DT, bool PASS_A, bool FUSE, bool DENSE = false>
 __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ H0,
     long T_len, int Hh, int Dv, int K, SegArgs sg, const unsigned long long* rmask,
     const float* ralpha, float* __restrict__ o, float* __restrict__ H_out, const T* __restrict__ z,
     const float* __restrict__ f, int32_t* __restrict__ idx_out) {
     static_assert(!FUSE || PASS_A, "only the first pass routes");
+    static_assert(!(FUSE && DENSE), "dense mode has no route");
     typedef Pol<T> P;
     typedef typename P::E E;
     typedef typename P::frag frag;
@@ -638,6 +642,7 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     const float* abase = ralpha + bh * T_pad * K;
     const unsigned long long* mbase = rmask + bh * T_pad * MW;
     auto issue_route = [&](long c, float* dA, unsigned long long* dM) {
+        if constexpr (DENSE) return;
         const char* ab = reinterpret_cast<const char*>(abase + c * C * K);
         const char* mb = reinterpret_cast<const char*>(mbase + c * C * MW);
         const int na = C * K * 4, nm = C * MW * 8;
@@ -649,9 +654,12 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     // ---- q and k pieces of the decay-product pass: token tl, SPL slots from s0
     struct Seg {
         uint32_t wd[NWD];
+        uint32_t zw[DENSE ? NWD : 1];  // dense mode, the k piece: the same slots of z, and f
+        float f;
     };
     const T* qbase = q + (b * T_len * rstride + h) * M + s0;
     const T* kbase = k + (b * T_len * rstride + h) * M + s0;
+    const T* zbase = z + (b * T_len * rstride + h) * M + s0;
     auto load_piece = [&](const T* src, Seg& s) {
         if constexpr (NWD % 4 == 0) {
 #pragma unroll
@@ -669,20 +677,25 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
     // (lanes past the chunk or the sequence get zeros; they load a valid row and select, so
     // the pieces are never assigned under a branch and stay in registers)
     // number of load instructions load_qk issues
-    constexpr int NQK = (NWD % 4 == 0 ? NWD / 4 : 1) * (PASS_A ? 1 : 2);
+    constexpr int NQK = (NWD % 4 == 0 ? NWD / 4 : 1) * (PASS_A ? 1 : 2) + (DENSE ? (NWD % 4 == 0 ? NWD / 4 : 1) + 1 : 0);
     auto load_qk = [&](long c, Seg& qs, Seg& ks) {
         // after every direct load of the phase: the waits for those skip these NQK loads
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const long t = c * C + tl;
         const bool ok = tl < C && t < T_len;
         const long row = (ok ? t : 0) * rstride * M;
-        Seg x, y;
+        Seg x, y, zz;
         load_piece(kbase + row, x);
         if (!PASS_A) load_piece(qbase + row, y);
+        if constexpr (DENSE) {
+            load_piece(zbase + row, zz);
+            ks.f = f[(b * T_len + (ok ? t : 0)) * rstride + h];
+        }
 #pragma unroll
         for (int p = 0; p < NWD; ++p) {
             ks.wd[p] = ok ? x.wd[p] : 0u;
             qs.wd[p] = PASS_A ? 0u : ok ? y.wd[p] : 0u;
+            if constexpr (DENSE) ks.zw[p] = zz.wd[p];
         }
     };
     auto unpack = [&](const Seg& s, float (&x)[SPL]) {
@@ -723,6 +736,27 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
         }
     };
 
+    // ---- dense mode: every slot's alpha from z and f of the lane's token (1 past the sequence)
+    auto gather_dense = [&](const Seg& ks, int nvalid, float (&al)[SPL]) {
+        float zf[SPL];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int p = 0; p < NWD; ++p) {
+                zf[2 * p] = __uint_as_float(ks.zw[p] << 16);
+                zf[2 * p + 1] = __uint_as_float(ks.zw[p] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < NWD; ++p) zf[p] = __uint_as_float(ks.zw[p]);
+        }
+        const bool in = tl < nvalid;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const float sc = sigmoidf_dev(zf[j]);
+            al[j] = (in && sc > 0.0f) ? __expf(sc * ks.f) : 1.0f;
+        }
+    };
+
     // ---- decay products, Qh = q o E and Kh = k (1 - alpha) / E (0 where alpha = 1) of
     // chunk c into buffer NB.  E is an inclusive product scan across the lanes of the clamped
     // alphas.  Also the per-slot E at the chunk end and the flag of a product that left the
@@ -738,7 +772,8 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
         // loads issued next
         wait_vm<0>();
         pre();
-        gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
+        if constexpr (DENSE) gather_dense(ks, valid_rows(c), al);
+        else gather(NB ? rA1 : rA0, NB ? rM1 : rM0, valid_rows(c), al);
         mid();
 #pragma unroll
         for (int j = 0; j < SPL; ++j) Ev[j] = clamp_alpha(al[j]);
@@ -984,9 +1019,15 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
         const T* rvc = CUR ? rv1 : rv0;
         if constexpr (DP) {
             float al[SPL], x[SPL];
-            gather(CUR ? rA1 : rA0, CUR ? rM1 : rM0, nvalid, al);
             Seg qs2, ks2;
-            load_qk(c, qs2, ks2);
+            if constexpr (DENSE) {
+                load_qk(c, qs2, ks2);
+                wait_vm<0>();
+                gather_dense(ks2, nvalid, al);
+            } else {
+                gather(CUR ? rA1 : rA0, CUR ? rM1 : rM0, nvalid, al);
+                load_qk(c, qs2, ks2);
+            }
             if (LPT == 2 || C == 64 || lane < C) {
                 Pol<float>::template put_row<SPL>(xa, 0, tl * M + s0, al);
                 unpack(ks2, x);
@@ -1254,9 +1295,31 @@ namespace rsm {
 template <typename T, int M, int C, int DT>
 static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long B, long T_len, long Hh, int Dv,
                        int K, const SegArgs& sg, const unsigned long long* rmask, const float* ralpha, float* o,
-                       float* H_out, const void* zr, const float* f, int32_t* idx_out, bool fuse, hipStream_t s) {
+                       float* H_out, const void* zr, const float* f, int32_t* idx_out, bool fuse, bool dense,
+                       hipStream_t s) {
     const long tiles = B * Hh * (Dv / DT);
     const T* z = static_cast<const T*>(zr);
+    // every slot every token (K = M, default router; bf16 at M = 128, the dense case of the
+    // router-limit sweep): both passes form the alphas from z and f, nothing routed
+    if constexpr (M == 128 && std::is_same<T, bf16_t>::value) {
+        if (dense) {
+            if (sg.S > 1) {
+                hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false, true>), dim3(unsigned(tiles * (sg.S - 1))),
+                                   dim3(64 * scan_waves<T, true, M>()), 0, s, q, k, v, H0, T_len, int(Hh), Dv, K, sg,
+                                   rmask, ralpha, o, H_out, z, f, idx_out);
+                if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
+                if (sg.S > kFoldMax + 1 || M > 128) {
+                    const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);
+                    if (st != RSM_OK) return st;
+                }
+            }
+            hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, false, false, true>), dim3(unsigned(tiles * sg.S)),
+                               dim3(64 * scan_waves<T, false, M>()), 0, s, q, k, v, H0, T_len, int(Hh), Dv, K, sg, rmask,
+                               ralpha, o, H_out, z, f, idx_out);
+            return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
+        }
+    }
+    if (dense) return RSM_ERR_UNSUPPORTED;
     if (sg.S > 1) {
         bool routed = false;
         if constexpr (std::is_same<T, bf16_t>::value && M <= 128) {  // fp32 rows would spill in the pass
@@ -1309,7 +1372,7 @@ static int dispatch_dt(int DT, const ScanArgs& a) {
     const T *q = static_cast<const T*>(a.q), *k = static_cast<const T*>(a.k), *v = static_cast<const T*>(a.v);
 #define RSM_SCAN(DTV) \
     return launch_scan<T, M, C, DTV>(q, k, v, a.H0, a.B, a.T_len, a.Hh, a.Dv, a.K, a.sg, a.rmask, a.ralpha, a.o, \
-                                     a.H_out, a.z, a.f, a.idx_out, a.fuse_route, a.s)
+                                     a.H_out, a.z, a.f, a.idx_out, a.fuse_route, a.dense, a.s)
     constexpr int cap = (sizeof(T) == 4 ? 64 : 128) / (M >= 128 ? 2 : 1);  // (M = 256: 64, bf16 only)
     switch (DT) {
         case 16: RSM_SCAN(16);

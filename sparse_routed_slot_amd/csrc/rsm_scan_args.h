@@ -36,6 +36,9 @@ struct ScanArgs {
     const float* f;
     int32_t* idx_out;
     bool fuse_route;
+    // every slot every token (K = M, default router): no route, the passes form the alphas
+    // from z and f (bf16, M = 128)
+    bool dense;
 };
 
 // Between the two passes: dH_s <- H_start(s+1) = diag(E_s) H_start(s) + dH_s for s = 0 .. S-2,
