@@ -1304,9 +1304,15 @@ static int launch_scan(const T* q, const T* k, const T* v, const float* H0, long
     if constexpr (M == 128 && std::is_same<T, bf16_t>::value) {
         if (dense) {
             if (sg.S > 1) {
-                hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false, true>), dim3(unsigned(tiles * (sg.S - 1))),
-                                   dim3(64 * scan_waves<T, true, M>()), 0, s, q, k, v, H0, T_len, int(Hh), Dv, K, sg,
-                                   rmask, ralpha, o, H_out, z, f, idx_out);
+                if (C >= 32 && Dv == DT)  // the segment-state pass, its alphas from z and f
+                    hipLaunchKernelGGL((seg_state_kernel<M, C >= 32 ? C : 32, DT, false, true>),
+                                       dim3(unsigned(B * Hh * (sg.S - 1))), dim3(512), 0, s, k, v, z, f, T_len,
+                                       int(Hh), Dv, K, sg, const_cast<unsigned long long*>(rmask),
+                                       const_cast<float*>(ralpha), idx_out);
+                else
+                    hipLaunchKernelGGL((fwd_scan_kernel<T, M, C, DT, true, false, true>),
+                                       dim3(unsigned(tiles * (sg.S - 1))), dim3(64 * scan_waves<T, true, M>()), 0, s, q,
+                                       k, v, H0, T_len, int(Hh), Dv, K, sg, rmask, ralpha, o, H_out, z, f, idx_out);
                 if (hipGetLastError() != hipSuccess) return RSM_ERR_HIP;
                 if (sg.S > kFoldMax + 1 || M > 128) {
                     const int st = seg_fold_launch(H0, sg, B * Hh, M, Dv, s);

@@ -40,7 +40,9 @@ constexpr int seg_round_one() {
     return r > 512 ? r : 512;
 }
 
-template <int M, int C, int DT, bool ONE>
+// DENSE (K = M, default router): no routing; each wave forms its tokens' alphas from z and f
+// (loaded two steps ahead like k), and the grid has no route-only workgroups.
+template <int M, int C, int DT, bool ONE, bool DENSE = false>
 __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                         const bf16_t* __restrict__ z, const float* __restrict__ f,
                                                         long T_len, int Hh, int Dv, int K, SegArgs sg,
@@ -77,14 +79,15 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     __shared__ __align__(16) float sB1[NW * 64 * SPL];  // odd steps
 
     const int nseg = sg.S - 1;
-    const long heads = long(gridDim.x) / sg.S;   // nseg segment workgroups + 1 routing one per head
+    // nseg segment workgroups per head, + 1 routing one (not in dense mode)
+    const long heads = long(gridDim.x) / (DENSE ? nseg : sg.S);
     const long nblk = heads * nseg;
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const long T_pad = sg.nC * C;
     const long seglen = long(sg.cps) * C;
 
-    if (long(blockIdx.x) >= nblk) {  // route the last segment of one head (read by the second pass only)
+    if (!DENSE && long(blockIdx.x) >= nblk) {  // route the last segment of one head (read by the second pass only)
         const long bh = long(blockIdx.x) - nblk;
         const long hb = bh / Hh, hh = bh % Hh;
         for (long t = long(nseg) * seglen + tid; t < T_len; t += NT)
@@ -131,6 +134,22 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     for (int r = 0; r < SPL; ++r) carry[r] = 1.0f;
     float al[2][TPW][SPL], rl[2][TPW][SPL];  // this wave's alphas and in-block exclusive suffix products
     float kx[4][TPW][SPL];                    // k of this wave's tokens, one set per step modulo 4
+    // dense mode: z of this wave's tokens and f (lane e % TPW holds token e's), per step modulo 4
+    float zx[DENSE ? 4 : 1][TPW][SPL], fx[DENSE ? 4 : 1];
+    const uint16_t* zb16 = reinterpret_cast<const uint16_t*>(z) + rowbase * M;
+    auto load_zf = [&](long c, float (&zc)[TPW][SPL], float& fc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < TPW; ++e) {
+            const long t = c * C + w * TPW + e;
+#pragma unroll
+            for (int r = 0; r < SPL; ++r) {
+                const int slot = lane + 64 * r;
+                const uint16_t x = zb16[t * rstride * M + (slot < M ? slot : M - 1)];
+                zc[e][r] = __uint_as_float(uint32_t(x) << 16);
+            }
+        }
+        fc = f[rowbase + (c * C + w * TPW + (lane % TPW)) * rstride];
+    };
 
     // W rows past the slot count stay zero (never read); clear once
     for (int i = tid; i < int(sizeof(sW0)) / 16; i += NT) {
@@ -154,9 +173,23 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
 
     // ---- phase 1 of chunk c: alphas of this wave's tokens and their in-block suffix products;
     // the block product goes to sB
-    auto phase1 = [&](auto nb, long c) __attribute__((always_inline)) {
+    auto phase1 = [&](auto nb, long c, const float (&zc)[TPW][SPL], float fc) __attribute__((always_inline)) {
         constexpr int NB = decltype(nb)::value;
         float* sB = NB ? sB1 : sB0;
+        float a[TPW][SPL];
+        bool sel[TPW][SPL];
+        if constexpr (DENSE) {  // every slot: alpha = exp(sigmoid(z) f), as the router forms it
+#pragma unroll
+            for (int e = 0; e < TPW; ++e) {
+                const float fe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fc), e));  // token e's f
+#pragma unroll
+                for (int r = 0; r < SPL; ++r) {
+                    const float sc = sigmoidf_dev(zc[e][r]);
+                    sel[e][r] = true;
+                    a[e][r] = sc > 0.0f ? __expf(sc * fe) : 1.0f;
+                }
+            }
+        } else {
         const int tl0 = int(c * C - rl0) + w * TPW;  // round-local index of this wave's first token
         // every LDS read first (masks, then the list entries), then the arithmetic
         unsigned long long m[TPW][MW];
@@ -164,8 +197,6 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
         for (int e = 0; e < TPW; ++e)
 #pragma unroll
             for (int wd = 0; wd < MW; ++wd) m[e][wd] = sMask[(tl0 + e) * MW + wd];
-        float a[TPW][SPL];
-        bool sel[TPW][SPL];
 #pragma unroll
         for (int e = 0; e < TPW; ++e)
 #pragma unroll
@@ -175,6 +206,7 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
                 sel[e][r] = (mw >> lane) & 1ull;
                 a[e][r] = sList[(tl0 + e) * K + (below < K ? below : K - 1)];
             }
+        }
         float run[SPL];
 #pragma unroll
         for (int r = 0; r < SPL; ++r) run[r] = 1.0f;
@@ -286,22 +318,32 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     auto step = [&](auto ph, long s) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;  // s % 4
         const long c = c_last - s;
-        if constexpr (!ONE)
+        if constexpr (!ONE && !DENSE)
             if (s > 0 && s < nsteps && c * C + C == rl0) route_round(round_lo(c), rl0 - round_lo(c));  // next round
         const long cv = c > c_first ? c : c_first, ck = c - 1 > c_first ? c - 1 : c_first;
         constexpr int PV = (PH + 2) & 3;
         issue_v(cv, PV == 0 ? rv0 : PV == 1 ? rv1 : PV == 2 ? rv2 : rv3);
         load_k(ck, kx[PV]);
+        if constexpr (DENSE) {  // z and f of chunk c-2, read by its phase 1 at step s+2
+            const long cz = c - 2 > c_first ? c - 2 : c_first;
+            load_zf(cz, zx[PV], fx[PV]);
+        }
         if (s >= 2 && s <= nsteps + 1) mfma(ph);
         if (s >= 1 && s <= nsteps) phase2(std::integral_constant<int, (PH + 1) & 1>{}, kx[PH]);
-        if (s < nsteps) phase1(std::integral_constant<int, PH & 1>{}, c);
+        if (s < nsteps) phase1(std::integral_constant<int, PH & 1>{}, c, zx[DENSE ? PH : 0], fx[DENSE ? PH : 0]);
         // what this step issued may stay in flight; everything before it has landed
-        if constexpr (EVEN) wait_vm<NI + TPW * SPL>();
+        constexpr int NV = NI + TPW * SPL + (DENSE ? TPW * SPL + 1 : 0);  // vector loads issued this step
+        if constexpr (EVEN) wait_vm<NV>();
         else wait_vm<0>();
         wg_barrier();
     };
 
-    route_round(round_lo(c_last), t_hi - round_lo(c_last));
+    if constexpr (DENSE) {
+        load_zf(c_last, zx[0], fx[0]);                                      // read at step 0
+        load_zf(c_last - 1 > c_first ? c_last - 1 : c_first, zx[1], fx[1]);  // read at step 1
+    } else {
+        route_round(round_lo(c_last), t_hi - round_lo(c_last));
+    }
     load_k(c_last, kx[1]);  // read at step 1
     for (long s = 0; s < nsteps + 2; s += 4) {
         step(std::integral_constant<int, 0>{}, s);

@@ -108,6 +108,11 @@ SMALL = [
     ("bf16", 1, 70, 1, 64, 256, 16, 16, True),
     ("f32", 1, 130, 2, 32, 32, 32, 64, True),
     ("bf16", 3, 1, 2, 64, 128, 16, 64, True),
+    # K = M = 128, bf16: the dense mode (alphas from z and f in the passes, no route):
+    # 2 segments with the in-pass fold, 8 with the fold kernel, one segment, a ragged tail
+    ("bf16", 1, 130, 4, 128, 64, 128, 64, True),
+    ("bf16", 1, 1000, 1, 128, 64, 128, 64, True),
+    ("bf16", 64, 40, 4, 128, 64, 128, 32, False),
 ]
 
 
