@@ -33,9 +33,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("variant", [False, True], ids=["default_router", "softmax_norm_noise_fslot"])
-def test_forward_graph_replays(rsm, variant):
-    B, T, Hh, M, Dv, K, C = 2, 300, 2, 64, 128, 16, 64
+@pytest.mark.parametrize("variant,M,Dv,K", [(False, 64, 128, 16), (True, 64, 128, 16), (False, 128, 64, 128),
+                                             (False, 256, 256, 32)],
+                         ids=["default_router", "softmax_norm_noise_fslot", "dense_m128", "chunked_m256"])
+def test_forward_graph_replays(rsm, variant, M, Dv, K):
+    B, T, Hh, C = 2, 300, 2, 64
     log(f"graph forward B{B} T{T} Hh{Hh} M{M} Dv{Dv} K{K} C{C} variant={variant}")
     d = gen.make_inputs(B, T, Hh, M, Dv, "bf16", seed=21, h0=True)
     t = dev_inputs(d, "cuda")
