@@ -13,39 +13,43 @@ __global__ void copy_state_kernel(const float* __restrict__ H0, float* __restric
     if (i < n) H_out[i] = H0 ? H0[i] : 0.0f;
 }
 
-// Segment fold (see seg_fold_launch): one thread per 4 consecutive columns of a state row;
-// the segments are walked in order, their (E, dH) read a batch at a time ahead of use.
+// Segment fold (see seg_fold_launch): one thread per W consecutive columns of a state row
+// (W = 4, or 1 when there are too few float4 of state to fill the chip); the segments are
+// walked in order, their (E, dH) read a batch at a time ahead of use.
 // keep: a row whose product E is 1 (untouched in the segment, so its dH is zero) keeps its
 // bits; otherwise every row is folded.
+template <int W>
 __global__ void seg_fold_kernel(const float* __restrict__ H0, float* __restrict__ dH, const float* __restrict__ dE,
-                                long n4, int S, int M, int Dv, int keep) {
+                                long nw, int S, int M, int Dv, int keep) {
     constexpr int NB = 8;
-    for (long idx = long(blockIdx.x) * blockDim.x + threadIdx.x; idx < n4; idx += long(gridDim.x) * blockDim.x) {
-        const long e0 = idx * 4;
+    typedef float vec __attribute__((ext_vector_type(W)));
+    for (long idx = long(blockIdx.x) * blockDim.x + threadIdx.x; idx < nw; idx += long(gridDim.x) * blockDim.x) {
+        const long e0 = idx * W;
         const int d = int(e0 % Dv);
         const long row = e0 / Dv;  // bh * M + i
         const long bh = row / M;
         const int i = int(row % M);
-        float4 hv = H0 ? *reinterpret_cast<const float4*>(H0 + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vec hv = H0 ? *reinterpret_cast<const vec*>(H0 + e0) : vec(0.0f);
         for (int s0 = 0; s0 < S - 1; s0 += NB) {
             float e[NB];
-            float4 x[NB];
+            vec x[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 if (s0 + j < S - 1) {
                     const long r = (bh * (S - 1) + s0 + j) * M + i;
                     e[j] = dE[r];
-                    x[j] = *reinterpret_cast<const float4*>(dH + r * Dv + d);
+                    x[j] = *reinterpret_cast<const vec*>(dH + r * Dv + d);
                 }
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 if (s0 + j < S - 1) {
                     const long r = (bh * (S - 1) + s0 + j) * M + i;
-                    if (!keep || e[j] != 1.0f)  // rows untouched in the segment keep their bits
-                        hv = make_float4(fmaf(e[j], hv.x, x[j].x), fmaf(e[j], hv.y, x[j].y), fmaf(e[j], hv.z, x[j].z),
-                                         fmaf(e[j], hv.w, x[j].w));
-                    *reinterpret_cast<float4*>(dH + r * Dv + d) = hv;
+                    if (!keep || e[j] != 1.0f) {  // rows untouched in the segment keep their bits
+#pragma unroll
+                        for (int c = 0; c < W; ++c) hv[c] = fmaf(e[j], hv[c], x[j][c]);
+                    }
+                    *reinterpret_cast<vec*>(dH + r * Dv + d) = hv;
                 }
             }
         }
@@ -59,10 +63,16 @@ __global__ void idx_iota_kernel(int32_t* __restrict__ idx, long n, int M) {
 }
 
 int seg_fold_launch(const float* H0, const SegArgs& sg, long BH, int M, int Dv, hipStream_t stream, bool keep) {
-    const long n4 = BH * M * Dv / 4;
-    const long blocks = (n4 + 255) / 256;
-    hipLaunchKernelGGL(seg_fold_kernel, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, H0, sg.dH,
-                       sg.dE, n4, sg.S, M, Dv, keep ? 1 : 0);
+    const long n = BH * M * Dv;
+    if (n / 4 >= 65536) {  // enough float4 of state for 256 blocks of 256 threads
+        const long blocks = (n / 4 + 255) / 256;
+        hipLaunchKernelGGL(seg_fold_kernel<4>, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, H0,
+                           sg.dH, sg.dE, n / 4, sg.S, M, Dv, keep ? 1 : 0);
+    } else {
+        const long blocks = (n + 255) / 256;
+        hipLaunchKernelGGL(seg_fold_kernel<1>, dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, H0,
+                           sg.dH, sg.dE, n, sg.S, M, Dv, keep ? 1 : 0);
+    }
     return hipGetLastError() == hipSuccess ? RSM_OK : RSM_ERR_HIP;
 }
 
