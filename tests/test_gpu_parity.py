@@ -191,16 +191,16 @@ def test_forward_split_sequence_resumes(rsm):
     check_close(H2.cpu().numpy(), H.cpu().numpy().astype(np.float64), scale, TOL["bf16"], "split H")
 
 
-@pytest.mark.parametrize("case", [("bf16", 1, 8192, 3, 64, 128), ("bf16", 8, 1024, 8, 64, 128),
-                                  ("bf16", 2, 640, 2, 64, 128), ("f32", 1, 2048, 2, 32, 64)],
+@pytest.mark.parametrize("case", [("bf16", 1, 8192, 3, 64, 128, 16), ("bf16", 8, 1024, 8, 64, 128, 16),
+                                  ("bf16", 2, 640, 2, 64, 128, 16), ("f32", 1, 2048, 2, 32, 64, 16),
+                                  ("bf16", 1, 2048, 2, 128, 64, 128), ("bf16", 1, 1500, 2, 256, 128, 32)],
                          ids=lambda c: "-".join(map(str, c)))
 def test_forward_inplace_state_with_segments(rsm, case):
     """H_out is the H0 buffer while the sequence is cut into segments: workgroups of early
     segments may start after the last segment's workgroup has written H_out, so the call
     must read the initial state from a copy (128 segments folded by the fold kernel; 4
-    folded inside the second pass; 5; fp32)."""
-    dtype, B, T, Hh, M, Dv = case
-    K = 16 if M >= 32 else 4
+    folded inside the second pass; 5; fp32; the dense mode at M = 128; chunked M = 256)."""
+    dtype, B, T, Hh, M, Dv, K = case
     log(f"in-place state with segments {case}")
     d = gen.make_inputs(B, T, Hh, M, Dv, dtype, seed=zlib.crc32(repr(case).encode()) % 1000, h0=True)
     t = dev_inputs(d, "cuda")
