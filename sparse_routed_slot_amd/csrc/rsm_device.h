@@ -179,17 +179,13 @@ __device__ __forceinline__ void bitonic_merge_desc16(U (&kv)[N], const int o) {
         }
 }
 
-// Threshold packed key of a row for K <= 16: the K-th largest of its M distinct packed keys.
-// Each group of 16 keys is sorted descending by a bitonic network; groups are then merged
-// pairwise keeping only the top 16 (the elementwise maximum of one sorted list and the other
-// reversed holds the top 16 of the union as a bitonic sequence, which a bitonic merge sorts).
-template <typename T, int M>
-__device__ __forceinline__ typename RowKey<T>::type row_threshold16(const float (&x)[M], int K) {
-    typedef typename RowKey<T>::type U;
+// K-th largest (K <= 16) of M keys, repeated keys counted (kv is overwritten).  Each group
+// of 16 keys is sorted descending by a bitonic network; groups are then merged pairwise
+// keeping only the top 16 (the elementwise maximum of one sorted list and the other reversed
+// holds the top 16 of the union as a bitonic sequence, which a bitonic merge sorts).
+template <typename U, int M>
+__device__ __forceinline__ U topk16_threshold(U (&kv)[M], int K) {
     static_assert(M % 16 == 0, "groups of 16");
-    U kv[M];
-#pragma unroll
-    for (int i = 0; i < M; ++i) kv[i] = RowKey<T>::make(x[i], i);
 #pragma unroll
     for (int g = 0; g < M; g += 16) {
 #pragma unroll
@@ -223,6 +219,60 @@ __device__ __forceinline__ typename RowKey<T>::type row_threshold16(const float 
 #pragma unroll
     for (int r = 1; r < 16; ++r) th = (r == K - 1) ? kv[r] : th;
     return th;
+}
+
+// Threshold packed key of a row for K <= 16: the K-th largest of its M distinct packed keys.
+template <typename T, int M>
+__device__ __forceinline__ typename RowKey<T>::type row_threshold16(const float (&x)[M], int K) {
+    typedef typename RowKey<T>::type U;
+    U kv[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) kv[i] = RowKey<T>::make(x[i], i);
+    return topk16_threshold<U, M>(kv, K);
+}
+
+// Selection mask of the K <= 16 largest fp32 values of a row, ties to the lower slot, with
+// 32-bit keys of the values alone (half the width of value-and-slot keys): the K-th largest
+// value key (repeats counted) is the threshold; every slot above it is selected, and of the
+// slots equal to it the lowest ones up to K in all.  The same selection as ranking the
+// packed (value, inverted slot) keys.
+template <int M>
+__device__ __forceinline__ void select16_f32(const float (&x)[M], int K, unsigned long long (&mk)[(M + 63) / 64]) {
+    constexpr int MW = (M + 63) / 64;
+    uint32_t key[M], kv[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) kv[i] = key[i] = order_key<32>(x[i]);
+    const uint32_t th = topk16_threshold<uint32_t, M>(kv, K);
+    int cnt = 0;
+#pragma unroll
+    for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+        if (key[i] >= th) mk[i >> 6] |= 1ull << (i & 63);
+#pragma unroll
+    for (int wd = 0; wd < MW; ++wd) cnt += __popcll(mk[wd]);
+    if (cnt > K) {  // slots equal to the threshold beyond the K-th: keep the lowest of them
+        unsigned long long gt[MW];
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) gt[wd] = 0ull;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            if (key[i] > th) gt[i >> 6] |= 1ull << (i & 63);
+        int need = K;
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) need -= __popcll(gt[wd]);
+#pragma unroll
+        for (int wd = 0; wd < MW; ++wd) {
+            unsigned long long eq = mk[wd] & ~gt[wd], sel = 0ull;
+            while (need > 0 && eq != 0ull) {
+                const unsigned long long lb = eq & (~eq + 1ull);
+                sel |= lb;
+                eq ^= lb;
+                --need;
+            }
+            mk[wd] = gt[wd] | sel;
+        }
+    }
 }
 
 // Threshold packed key of a row: the K-th largest of its M packed keys (K uniform).

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
 // the cases the pages name besides the default router).  Same outputs and row mapping as
 // route_rows_kernel.  Without noise the selection is that of the default router (the
 // scores are increasing in the logits), so it uses the same top-K; with noise the logits
-// z + g (one fp32 add) are ranked with packed 64-bit keys (value, then inverted slot).
+// z + g (one fp32 add) are ranked by value with 32-bit keys, ties to the lower slot (K <= 16),
+// or with packed 64-bit keys (value, then inverted slot) above that.
 // The selected slots are walked in ascending order as in route_rows_kernel, their logits
 // (and noise) read again from the rows just loaded; the softmax denominator is a sum over
 // the whole row.
@@ -103,6 +104,8 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
             constexpr bool kPacked = std::is_same<T, bf16_t>::value && M >= 32 && SMALLK;
             if constexpr (kPacked && !NOISY) {
                 pk_select<M>(x.r, K, mk);
+            } else if constexpr (SMALLK && (NOISY || std::is_same<T, float>::value)) {
+                select16_f32<M>(v, K, mk);  // fp32 values: the noisy logits, or fp32 rows
             } else if constexpr (!NOISY) {
                 U th;
                 if constexpr (SMALLK) th = row_threshold16<T, M>(v, K);
@@ -111,9 +114,7 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
                 for (int i = 0; i < M; ++i)
                     if (RowKey<T>::make(v[i], i) >= th) mk[i >> 6] |= 1ull << (i & 63);
             } else {
-                typename RowKey<float>::type th;
-                if constexpr (SMALLK) th = row_threshold16<float, M>(v, K);
-                else th = row_threshold<float, M>(v, K);
+                typename RowKey<float>::type th = row_threshold<float, M>(v, K);
 #pragma unroll
                 for (int i = 0; i < M; ++i)
                     if (RowKey<float>::make(v[i], i) >= th) mk[i >> 6] |= 1ull << (i & 63);

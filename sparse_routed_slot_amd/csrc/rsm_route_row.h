@@ -241,27 +241,28 @@ __device__ __forceinline__ void route_row(const T* __restrict__ z, const float* 
     const float ft = kFwd ? f[row] : 0.0f;  // issued with the row: its latency overlaps the top-K
     const bool all = (K == M);
     constexpr bool kPacked = std::is_same<T, bf16_t>::value && M >= 32 && SMALLK;
-    U th = 0;
-    if (!all && !kPacked) {
-        float v[M];
-#pragma unroll
-        for (int i = 0; i < M; ++i) v[i] = x.val(i);
-        if constexpr (SMALLK) th = row_threshold16<T, M>(v, K);
-        else th = row_threshold<T, M>(v, K);
-    }
-
+    constexpr bool kValKey = std::is_same<T, float>::value && SMALLK;  // fp32 rows: 32-bit value keys
     // selected slots as a bit mask (bit i%64 of word i/64)
     constexpr int MW = (M + 63) / 64;
     unsigned long long mk[MW];
 #pragma unroll
     for (int wd = 0; wd < MW; ++wd) mk[wd] = 0ull;
+    U th = 0;
+    if (!all && !kPacked) {
+        float v[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) v[i] = x.val(i);
+        if constexpr (kValKey) select16_f32<M>(v, K, mk);
+        else if constexpr (SMALLK) th = row_threshold16<T, M>(v, K);
+        else th = row_threshold<T, M>(v, K);
+    }
     if (!all && kPacked) {
         if constexpr (kPacked) pk_select<M>(x.r, K, mk);
-    } else if (!all) {
+    } else if (!all && !kValKey) {
 #pragma unroll
         for (int i = 0; i < M; ++i)
             if (RowKey<T>::make(x.val(i), i) >= th) mk[i >> 6] |= 1ull << (i & 63);
-    } else {
+    } else if (all) {
 #pragma unroll
         for (int wd = 0; wd < MW; ++wd) mk[wd] = (M - 64 * wd >= 64) ? ~0ull : ((1ull << (M - 64 * wd)) - 1ull);
     }
