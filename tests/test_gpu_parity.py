@@ -95,6 +95,28 @@ def test_route_ties_and_signed_zeros(rsm, M, dtype):
         assert np.array_equal(idx.cpu().numpy(), ridx), f"K={K}"
 
 
+@pytest.mark.parametrize("M", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_noisy_ties_and_signed_zeros(rsm, M, dtype):
+    """Noisy logits z + g whose fp32 sums tie exactly (and are -0 or +0): the selection by
+    value with ties to the lower slot, K <= 16 (value keys with the tie fix-up) and above."""
+    log(f"noisy route ties M={M} {dtype}")
+    rng = np.random.default_rng(100 + M)
+    z = (rng.integers(-4, 5, size=(2, 40, 3, M)) * 0.25).astype(np.float32)
+    z[rng.random(z.shape) < 0.2] = -0.0
+    g = (rng.integers(-2, 3, size=z.shape) * 0.25).astype(np.float32)
+    g[rng.random(g.shape) < 0.2] = -0.0
+    z[0, 0, 0, :] = 0.5
+    g[0, 0, 0, :] = 0.0                                 # all sums equal
+    enc = gen.bf16_bits(z) if dtype == "bf16" else z
+    for K in sorted({1, 3, 8, 16, M // 2, M - 1} - {0}):
+        if K > M:
+            continue
+        idx, _ = rsm.route_topk(to_torch(enc, dtype, "cuda"), K, want_score=False, noise=torch.from_numpy(g).cuda())
+        ridx, _ = oracle.route_topk(gen.as_f64(enc, dtype), K, noise=g.astype(np.float64))
+        assert np.array_equal(idx.cpu().numpy(), ridx), f"K={K}"
+
+
 # ------------------------------------------------------------------------------- forward
 SMALL = [
     # dtype, B, T, Hh, M, Dv, K, C, H0
