@@ -63,21 +63,42 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
                                                            float* __restrict__ ralpha, RouterOpts op) {
     typedef typename RowKey<T>::type U;
     const int lane = threadIdx.x;
-    long row, t = 0, bh = 0;
-    if (kFwd) {
-        const long nbt = (T_len + 63) / 64;
-        bh = long(blockIdx.x) / nbt;
-        t = (long(blockIdx.x) % nbt) * 64 + lane;
-        if (t >= T_len) return;  // no cross-lane operations below
-        row = ((bh / Hh) * T_len + t) * Hh + bh % Hh;
-    } else {
-        row = long(blockIdx.x) * 64 + lane;
-        if (row >= n_rows) return;
+    // row of the workgroup's l-th lane, and whether it exists
+    const long nbt = (T_len + 63) / 64;
+    const long bh = kFwd ? long(blockIdx.x) / nbt : 0;
+    const long t0 = kFwd ? (long(blockIdx.x) % nbt) * 64 : 0;
+    auto row_of = [&](int l, bool& ok) {
+        if (kFwd) {
+            ok = t0 + l < T_len;
+            return ((bh / Hh) * T_len + (ok ? t0 + l : 0)) * Hh + bh % Hh;
+        }
+        ok = long(blockIdx.x) * 64 + l < n_rows;
+        return ok ? long(blockIdx.x) * 64 + l : 0l;
+    };
+    bool valid;
+    const long row = row_of(lane, valid);
+    const long t = t0 + lane;
+    // The noise rows (4*M contiguous bytes each) go through LDS: loaded row by row with
+    // consecutive lanes on consecutive 16-byte pieces, then each lane reads its own row (read
+    // directly, lane by lane, they made an uncoalesced stream).  One pad granule per LDS row.
+    constexpr bool kStage = NOISY && M <= 64;
+    constexpr int GPR = M / 4, GP = GPR + 1;
+    __shared__ float4 sg[kStage ? 64 * GP : 1];
+    if constexpr (kStage) {
+#pragma unroll
+        for (int it = 0; it < GPR; ++it) {
+            const int e = it * 64 + lane, rl = e / GPR, c = e % GPR;
+            bool ok;
+            const long r = row_of(rl, ok);
+            if (ok) sg[rl * GP + c] = reinterpret_cast<const float4*>(op.noise + r * M)[c];
+        }
+        __syncthreads();
     }
+    if (!valid) return;  // no cross-lane operations below
 
     RowRegs<T, M> x;
     x.load(z + row * M);
-    const float* grow = NOISY ? op.noise + row * M : nullptr;
+    const float* grow = !NOISY ? nullptr : kStage ? reinterpret_cast<const float*>(sg + lane * GP) : op.noise + row * M;
     constexpr int MW = (M + 63) / 64;
     unsigned long long mk[MW];
 #pragma unroll
