@@ -81,19 +81,25 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
     // The noise rows (4*M contiguous bytes each) go through LDS: loaded row by row with
     // consecutive lanes on consecutive 16-byte pieces, then each lane reads its own row (read
     // directly, lane by lane, they made an uncoalesced stream).  One pad granule per LDS row.
-    constexpr bool kStage = NOISY && M <= 64;
+    // The per-slot decay rates of the forward router (read at the K selected slots) likewise.
+    // (not both: two 17 KB tiles per wave leave room for four waves per CU, measured slower)
+    constexpr bool kStage = NOISY && M <= 64, kStageF = kFwd && M <= 64 && !NOISY;
     constexpr int GPR = M / 4, GP = GPR + 1;
     __shared__ float4 sg[kStage ? 64 * GP : 1];
-    if constexpr (kStage) {
+    __shared__ float4 sf[kStageF ? 64 * GP : 1];
+    auto stage = [&](float4* dst, const float* src) {
 #pragma unroll
         for (int it = 0; it < GPR; ++it) {
             const int e = it * 64 + lane, rl = e / GPR, c = e % GPR;
             bool ok;
             const long r = row_of(rl, ok);
-            if (ok) sg[rl * GP + c] = reinterpret_cast<const float4*>(op.noise + r * M)[c];
+            if (ok) dst[rl * GP + c] = reinterpret_cast<const float4*>(src + r * M)[c];
         }
-        __syncthreads();
-    }
+    };
+    const bool stage_f = kStageF && op.f_per_slot;  // uniform
+    if constexpr (kStage) stage(sg, op.noise);
+    if (stage_f) stage(sf, f);
+    if (kStage || stage_f) __syncthreads();
     if (!valid) return;  // no cross-lane operations below
 
     RowRegs<T, M> x;
@@ -161,7 +167,9 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
         for (int wd = 0; wd < MW; ++wd) rmask[orow * MW + wd] = mk[wd];
     }
     float* alist = kFwd ? ralpha + (bh * T_pad + (t - t % C)) * K + t % C : nullptr;  // entry n at alist[n*C]
-    const float* frow = kFwd ? (op.f_per_slot ? f + row * M : f + row) : nullptr;
+    const float* frow = !kFwd ? nullptr
+                        : stage_f ? reinterpret_cast<const float*>(sf + lane * GP)
+                        : op.f_per_slot ? f + row * M : f + row;
     auto emit = [&](int n, int i, float s) {
         if (kFwd) {
             const float fi = frow[op.f_per_slot ? i : 0];
