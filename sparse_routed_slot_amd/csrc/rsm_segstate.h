@@ -87,16 +87,22 @@ __global__ __launch_bounds__(512) void seg_state_kernel(const bf16_t* __restrict
     const long T_pad = sg.nC * C;
     const long seglen = long(sg.cps) * C;
 
+    // heads on XCDs as in the second pass: workgroups are dealt to the 8 XCDs round-robin, and
+    // the second pass gives XCD x the heads [x*heads/8, (x+1)*heads/8), so the route and the
+    // segment states it reads were written through the same L2
+    const bool xmap = nblk % 8 == 0 && heads % 8 == 0;
     if (!DENSE && long(blockIdx.x) >= nblk) {  // route the last segment of one head (read by the second pass only)
-        const long bh = long(blockIdx.x) - nblk;
+        const long r = long(blockIdx.x) - nblk;
+        const long bh = xmap ? (r % 8) * (heads / 8) + r / 8 : r;
         const long hb = bh / Hh, hh = bh % Hh;
         for (long t = long(nseg) * seglen + tid; t < T_len; t += NT)
             route_row<bf16_t, M, true, true>(z, f, (hb * T_len + t) * Hh + hh, bh, t, T_pad, K, C, idx_out, nullptr,
                                              rmask, ralpha);
         return;
     }
-    const long bh = long(blockIdx.x) / nseg;
-    const int seg = int(long(blockIdx.x) % nseg);
+    const long id = xmap ? (long(blockIdx.x) % 8) * (nblk / 8) + long(blockIdx.x) / 8 : long(blockIdx.x);
+    const long bh = id / nseg;
+    const int seg = int(id % nseg);
     const long hb = bh / Hh, hh = bh % Hh;
     const long t_lo = long(seg) * seglen, t_hi = t_lo + seglen;  // segments but the last are full
     const long rstride = long(Hh);
