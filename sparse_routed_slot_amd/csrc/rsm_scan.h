@@ -1167,7 +1167,7 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
             if (c_begin + 1 < c_end) issue_route(c_begin + 1, rA1, rM1);
             load_qk(c_begin + 1, qA, kA);
         }
-        if (DM && !PASS_A) {
+        auto load_start = [&]() __attribute__((always_inline)) {
             // Segment 0 starts from H0 (or zero).  Segment s > 0 starts from the state the
             // segments before it leave: with more than kFoldMax + 1 segments it was folded in
             // place of dH_{s-1} between the two passes; otherwise it is folded here, every
@@ -1240,7 +1240,12 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
                                 Hreg[j][I][r] = use ? fmaf(e, Hreg[j][I][r], xv[sj][j][I][r]) : Hreg[j][I][r];
                             }
             }
-        }
+        };
+        // With split roles the state waves load and fold their start state while the
+        // decay-product waves prepare the first chunk (its latency, a round trip per earlier
+        // segment, then overlaps that work); otherwise it comes first.
+        const bool late = SPLIT && c_begin < c_end;
+        if (DM && !PASS_A && !late) load_start();
         if (MP > M || CP > C) zero_qk();
         if (!PASS_A) zero16(sP, int(sizeof(sP)));
         if (c_begin < c_end) {
@@ -1251,6 +1256,7 @@ __global__ __launch_bounds__((64 * scan_waves<T, PASS_A, M>())) void fwd_scan_ke
                 prep(std::integral_constant<int, 0>{}, c_begin, qB, kB, Ev, [] {}, [] {});
                 prep_tail(std::integral_constant<int, 0>{}, Ev);
             }
+            if (DM && !PASS_A && late) load_start();
             wg_barrier();
         }
         for (long c = c_begin; c < c_end; c += 2) {
