@@ -49,6 +49,14 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Block index permuted so that a grid whose blocks run head-major (nblk = heads x blocks per
+// head) gives XCD x the heads [x*heads/8, (x+1)*heads/8), as the chunk scan does: workgroups
+// are dealt to the 8 XCDs round-robin, so data a kernel writes for a head is then read by
+// the scan through the same L2.  The identity unless the head count is a multiple of 8.
+__device__ __forceinline__ long xcd_head_major(long bid, long nblk, long heads) {
+    return heads % 8 == 0 ? (bid % 8) * (nblk / 8) + bid / 8 : bid;
+}
+
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
 // Number of set bits of m in lanes below the calling lane.

@@ -34,8 +34,9 @@ __global__ __launch_bounds__(64) void route_rows_kernel(const T* __restrict__ z,
     long row, t = 0, bh = 0;
     if (kFwd) {
         const long nbt = (T_len + 63) / 64;
-        bh = long(blockIdx.x) / nbt;
-        t = (long(blockIdx.x) % nbt) * 64 + lane;
+        const long id = xcd_head_major(blockIdx.x, gridDim.x, gridDim.x / nbt);
+        bh = id / nbt;
+        t = (id % nbt) * 64 + lane;
         if (t >= T_len) return;  // no cross-lane operations below
         row = ((bh / Hh) * T_len + t) * Hh + bh % Hh;
     } else {
@@ -65,8 +66,9 @@ __global__ __launch_bounds__(64) void route_rows_ex_kernel(const T* __restrict__
     const int lane = threadIdx.x;
     // row of the workgroup's l-th lane, and whether it exists
     const long nbt = (T_len + 63) / 64;
-    const long bh = kFwd ? long(blockIdx.x) / nbt : 0;
-    const long t0 = kFwd ? (long(blockIdx.x) % nbt) * 64 : 0;
+    const long bid = kFwd ? xcd_head_major(blockIdx.x, gridDim.x, gridDim.x / nbt) : long(blockIdx.x);
+    const long bh = kFwd ? bid / nbt : 0;
+    const long t0 = kFwd ? (bid % nbt) * 64 : 0;
     auto row_of = [&](int l, bool& ok) {
         if (kFwd) {
             ok = t0 + l < T_len;
@@ -307,7 +309,8 @@ __global__ __launch_bounds__(512) void route_chunk_wave_kernel(const T* __restri
     __shared__ unsigned long long sM[64 * MW];         // [t][MW]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const long nch = T_pad / C;
-    const long bh = long(blockIdx.x) / nch, c = long(blockIdx.x) % nch;
+    const long bid = xcd_head_major(blockIdx.x, gridDim.x, gridDim.x / nch);
+    const long bh = bid / nch, c = bid % nch;
     const long hb = bh / Hh, hh = bh % Hh;
     for (int tt = w; tt < C; tt += NWV) {
         const long t = c * C + tt;
